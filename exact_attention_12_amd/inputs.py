@@ -1,0 +1,174 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module draws random numbers and lays them out; it holds none of the
+attention arithmetic, so the GPU path and the CPU oracle can both read what
+it produces.
+
+Recipe (every tensor on the host first, so both sides see identical values):
+  seed = 1000 * config_id + t, with t = 0 for Q, 1 for K, 2 for V, 3 for the
+  context lengths, 4 for the block permutation, 5 for sampled rows, 6 for the
+  decode query;
+  numpy PCG64 ``standard_normal`` in fp32, times the config's factor, then one
+  round-to-nearest-even cast to the element type (``torch.Tensor.to``).
+"""
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+__all__ = ["FwdConfig", "FWD_CONFIGS", "DecodeConfig", "DECODE_CONFIG", "normal",
+           "fwd_inputs", "sample_rows", "decode_inputs"]
+
+
+@dataclass(frozen=True)
+class FwdConfig:
+    """One forward workload: [B, H, N, d] tensors of one element type."""
+    cid: int
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: torch.dtype
+    causal: bool
+    qk_factor: float = 1.0  # Q and K are drawn N(0,1) * qk_factor
+    name: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self) -> float:
+        """Matmul flop count 4*B*H*N^2*d, halved for causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def replace(self, **kw) -> "FwdConfig":
+        args = dict(cid=self.cid, B=self.B, H=self.H, N=self.N, d=self.d, dtype=self.dtype,
+                    causal=self.causal, qk_factor=self.qk_factor, name=self.name)
+        args.update(kw)
+        return FwdConfig(**args)
+
+
+FWD_CONFIGS = {
+    1: FwdConfig(1, 1, 1, 256, 64, torch.float32, False, 1.0, "B1 H1 N256 d64 fp32"),
+    2: FwdConfig(2, 4, 16, 2048, 64, torch.bfloat16, False, 1.0, "B4 H16 N2048 d64 bf16"),
+    3: FwdConfig(3, 2, 32, 8192, 128, torch.bfloat16, True, 1.0, "B2 H32 N8192 d128 bf16 causal"),
+    4: FwdConfig(4, 1, 8, 65536, 128, torch.bfloat16, True, 2.0,
+                 "B1 H8 N65536 d128 bf16 causal, Q,K x2"),
+}
+
+
+def normal(seed: int, shape, factor: float = 1.0, dtype=torch.float32) -> torch.Tensor:
+    """N(0,1) * factor drawn in fp32 from PCG64(seed), cast (RNE) to dtype; CPU tensor."""
+    x = np.random.default_rng(seed).standard_normal(size=tuple(shape), dtype=np.float32)
+    if factor != 1.0:
+        x *= np.float32(factor)
+    return torch.from_numpy(x).to(dtype)
+
+
+def fwd_inputs(cfg: FwdConfig):
+    """(q, k, v) CPU tensors [B, H, N, d] of cfg.dtype."""
+    shape = (cfg.B, cfg.H, cfg.N, cfg.d)
+    base = 1000 * cfg.cid
+    q = normal(base + 0, shape, cfg.qk_factor, cfg.dtype)
+    k = normal(base + 1, shape, cfg.qk_factor, cfg.dtype)
+    v = normal(base + 2, shape, 1.0, cfg.dtype)
+    return q, k, v
+
+
+def sample_rows(N: int, count: int = 256, seed: int = 5) -> np.ndarray:
+    """Sorted query rows: {0, 1, 127, 128, N-1} (where < N) plus random distinct rows."""
+    fixed = sorted({r for r in (0, 1, 127, 128, N - 1) if 0 <= r < N})
+    if count >= N:
+        return np.arange(N, dtype=np.int64)
+    rest = np.setdiff1d(np.arange(N, dtype=np.int64), np.array(fixed, dtype=np.int64))
+    extra = np.random.default_rng(seed).choice(rest, size=count - len(fixed), replace=False)
+    return np.sort(np.concatenate([np.array(fixed, dtype=np.int64), extra]))
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    """Paged single-query decode workload."""
+    cid: int = 5
+    num_seqs: int = 64
+    num_heads: int = 32
+    num_kv_heads: int = 32
+    head_size: int = 128
+    block_size: int = 16
+    num_blocks: int = 20000
+    ctx_lo: int = 512
+    ctx_hi: int = 4096
+    dtype: torch.dtype = torch.float16
+    name: str = "64 seqs, 32 heads, head 128, fp16, block 16, ctx U[512,4096], 20000-block pool"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_size)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return (self.ctx_hi + self.block_size - 1) // self.block_size
+
+    def replace(self, **kw) -> "DecodeConfig":
+        args = {f: getattr(self, f) for f in self.__dataclass_fields__}
+        args.update(kw)
+        return DecodeConfig(**args)
+
+
+DECODE_CONFIG = DecodeConfig()
+
+
+def decode_inputs(cfg: DecodeConfig = DECODE_CONFIG, context_lens=None):
+    """Paged-cache inputs as CPU tensors.
+
+    Returns dict(q [S,H,D], k_cache [NB,Hkv,D/x,BS,x], v_cache [NB,Hkv,D,BS],
+    block_tables [S, max_blocks] int32, context_lens [S] int32, max_context_len).
+    Context lengths are integers uniform in [ctx_lo, ctx_hi] (both inclusive)
+    unless given.  One seeded permutation of the pool hands each sequence its
+    next ceil(ctx/BS) blocks in order.  Every pool element that no context
+    token uses -- whole unused blocks and the slots past the end of a
+    sequence's last block -- is NaN, and unused table entries point at an
+    all-NaN block, so any read outside the context poisons the output.
+    """
+    S, H, Hkv, D, BS, NB = (cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size,
+                            cfg.block_size, cfg.num_blocks)
+    esize = torch.empty((), dtype=cfg.dtype).element_size()
+    x = 16 // esize
+    base = 1000 * cfg.cid
+    if context_lens is None:
+        ctx = np.random.default_rng(base + 3).integers(cfg.ctx_lo, cfg.ctx_hi + 1, size=S)
+    else:
+        ctx = np.asarray(context_lens, dtype=np.int64)
+    mb = max(1, cfg.max_blocks_per_seq, int((ctx.max() + BS - 1) // BS) if len(ctx) else 1)
+    nblk = (ctx + BS - 1) // BS
+    total = int(nblk.sum())
+    if total >= NB:
+        raise ValueError("pool of %d blocks cannot hold %d used blocks plus a NaN block"
+                         % (NB, total))
+    perm = np.random.default_rng(base + 4).permutation(NB)
+    nan_block = int(perm[-1])
+    tables = np.full((S, mb), nan_block, dtype=np.int32)
+    pos = 0
+    for s in range(S):
+        n = int(nblk[s])
+        tables[s, :n] = perm[pos:pos + n]
+        pos += n
+    used = torch.from_numpy(perm[:total].astype(np.int64))
+
+    k_cache = torch.full((NB, Hkv, D // x, BS, x), float("nan"), dtype=cfg.dtype)
+    v_cache = torch.full((NB, Hkv, D, BS), float("nan"), dtype=cfg.dtype)
+    if total:
+        k_cache[used] = normal(base + 1, (total, Hkv, D // x, BS, x), 1.0, cfg.dtype)
+        v_cache[used] = normal(base + 2, (total, Hkv, D, BS), 1.0, cfg.dtype)
+    # NaN the slots past each context's end inside its last block
+    for s in range(S):
+        n, c = int(nblk[s]), int(ctx[s])
+        if n and c % BS:
+            blk = int(tables[s, n - 1])
+            k_cache[blk, :, :, c % BS:, :] = float("nan")
+            v_cache[blk, :, :, c % BS:] = float("nan")
+    q = normal(base + 6, (S, H, D), 1.0, cfg.dtype)
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=torch.from_numpy(tables),
+                context_lens=torch.from_numpy(ctx.astype(np.int32)),
+                max_context_len=int(ctx.max()) if len(ctx) else 0)

@@ -1,0 +1,215 @@
+"""The exact-attention ORACLE (fp64, CPU) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU
+baseline leg may import this package.  The GPU library and its Python binding
+never import it, and it shares no code with them.
+
+``oracle.c`` holds the arithmetic (plain loops, fp64, libm exp/log, sums in
+ascending index order); this module builds it with gcc and wraps it with
+ctypes.  Inputs are read in their storage type (fp32 / bf16 / fp16 / fp64)
+and widened exactly inside the C code.
+
+Functions (each cites the page passages it follows in ``oracle.c``):
+  attention(q, k, v, scale, causal, rows=None)        dense definition
+  probs(q, k, scale, causal)                          the full P matrix
+  tiled_fa1 / tiled_fa2(q, k, v, scale, causal, Br, Bc)
+                                                      the online recurrence in
+                                                      both loop orders
+  paged_decode(...), paged_decode_partitioned(...)    single-query decode
+  widen(x)                                            exact fp64 view
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OR_F32, OR_BF16, OR_F16, OR_F64 = 0, 1, 2, 3
+_CODES = {torch.float32: OR_F32, torch.bfloat16: OR_BF16, torch.float16: OR_F16,
+          torch.float64: OR_F64}
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (no -ffast-math) and return its path."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra",
+           SRC, "-o", tmp, "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("oracle build failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        build()
+    lib = ctypes.CDLL(LIB)
+    vp, i, d, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int64
+    lib.oracle_widen.argtypes = [vp, i, i64, vp]
+    lib.oracle_attention.argtypes = [vp, vp, vp, i, i, i, i, i, d, i, vp, i64, vp, vp, i]
+    lib.oracle_probs.argtypes = [vp, vp, i, i, i, i, i, d, i, vp]
+    lib.oracle_tiled_fa1.argtypes = [vp, vp, vp, i, i, d, i, i, i, vp, vp]
+    lib.oracle_tiled_fa2.argtypes = [vp, vp, vp, i, i, d, i, i, i, vp, vp]
+    lib.oracle_paged_decode.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, d, vp, vp, i]
+    lib.oracle_paged_decode_partitioned.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, d, i,
+                                                    vp, vp, vp, vp, vp, i]
+    for name in ("oracle_widen", "oracle_attention", "oracle_probs", "oracle_tiled_fa1",
+                 "oracle_tiled_fa2", "oracle_paged_decode", "oracle_paged_decode_partitioned"):
+        getattr(lib, name).restype = i
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def _host(x):
+    """(contiguous CPU tensor, dtype code) for a torch tensor or numpy array."""
+    if isinstance(x, np.ndarray):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("expected a tensor or array")
+    x = x.detach().cpu().contiguous()
+    if x.dtype not in _CODES:
+        raise TypeError("unsupported dtype %s" % x.dtype)
+    return x, _CODES[x.dtype]
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if isinstance(t, torch.Tensor) else \
+        ctypes.c_void_p(t.ctypes.data)
+
+
+def _check(st, name):
+    if st != 0:
+        raise ValueError("%s rejected its arguments or ran out of memory" % name)
+
+
+def widen(x) -> np.ndarray:
+    """Exact fp64 values of x (decoded from its storage type by the oracle)."""
+    t, code = _host(x)
+    out = np.empty(t.numel(), dtype=np.float64)
+    _check(_load().oracle_widen(_p(t), code, t.numel(), _p(out)), "oracle_widen")
+    return out.reshape(tuple(t.shape))
+
+
+def attention(q, k, v, scale, causal, rows=None, nthreads=None):
+    """Dense attention on [B, H, N, d] inputs.
+
+    Returns (o [B, H, R, d], lse [B, H, R]) in fp64, R = len(rows) or N.
+    """
+    qt, code = _host(q)
+    kt, c2 = _host(k)
+    vt, c3 = _host(v)
+    if not (code == c2 == c3) or qt.shape != kt.shape or qt.shape != vt.shape or qt.dim() != 4:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape and dtype")
+    B, H, N, d = qt.shape
+    if rows is None:
+        rarr, R = None, N
+    else:
+        rarr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R = len(rarr)
+    o = np.empty((B, H, R, d), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    st = _load().oracle_attention(_p(qt), _p(kt), _p(vt), code, B, H, N, d, float(scale),
+                                  int(bool(causal)),
+                                  None if rarr is None else _p(rarr), R, _p(o), _p(lse),
+                                  nthreads or default_threads())
+    _check(st, "oracle_attention")
+    return o, lse
+
+
+def probs(q, k, scale, causal):
+    """Full P = softmax(scale Q K^T [+mask]) [B, H, N, N] fp64 (tiny inputs only)."""
+    qt, code = _host(q)
+    kt, c2 = _host(k)
+    if code != c2 or qt.shape != kt.shape or qt.dim() != 4:
+        raise ValueError("q, k must share one [B, H, N, d] shape and dtype")
+    B, H, N, d = qt.shape
+    P = np.empty((B, H, N, N), dtype=np.float64)
+    _check(_load().oracle_probs(_p(qt), _p(kt), code, B, H, N, d, float(scale),
+                                int(bool(causal)), _p(P)), "oracle_probs")
+    return P
+
+
+def _tiled(fn, q, k, v, scale, causal, Br, Bc):
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    N, d = q.shape
+    o = np.empty((N, d), dtype=np.float64)
+    lse = np.empty(N, dtype=np.float64)
+    _check(fn(_p(q), _p(k), _p(v), N, d, float(scale), int(bool(causal)), int(Br), int(Bc),
+              _p(o), _p(lse)), "oracle_tiled")
+    return o, lse
+
+
+def tiled_fa1(q, k, v, scale, causal, Br, Bc):
+    """FlashAttention-1 order (KV tiles outer) on one head: (o [N,d], lse [N])."""
+    return _tiled(_load().oracle_tiled_fa1, q, k, v, scale, causal, Br, Bc)
+
+
+def tiled_fa2(q, k, v, scale, causal, Br, Bc):
+    """FlashAttention-2 order (Q tiles outer, deferred normalisation) on one head."""
+    return _tiled(_load().oracle_tiled_fa2, q, k, v, scale, causal, Br, Bc)
+
+
+def _dec_args(q, k_cache, v_cache, block_tables, context_lens):
+    qt, code = _host(q)
+    kt, c2 = _host(k_cache)
+    vt, c3 = _host(v_cache)
+    if not (code == c2 == c3):
+        raise ValueError("q and caches must share a dtype")
+    bt = np.ascontiguousarray(torch.as_tensor(block_tables).cpu().numpy().astype(np.int32))
+    cl = np.ascontiguousarray(torch.as_tensor(context_lens).cpu().numpy().astype(np.int32))
+    S, H, D = qt.shape
+    Hkv, BS = kt.shape[1], kt.shape[3]
+    return qt, kt, vt, code, bt, cl, S, H, Hkv, D, BS, bt.shape[1]
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, nthreads=None):
+    """Unsplit paged decode: (out [S, H, D], lse [S, H]) fp64."""
+    qt, kt, vt, code, bt, cl, S, H, Hkv, D, BS, MB = _dec_args(q, k_cache, v_cache, block_tables,
+                                                               context_lens)
+    out = np.empty((S, H, D), dtype=np.float64)
+    lse = np.empty((S, H), dtype=np.float64)
+    st = _load().oracle_paged_decode(_p(qt), _p(kt), _p(vt), code, _p(bt), _p(cl), S, H, Hkv, D,
+                                     BS, MB, float(scale), _p(out), _p(lse),
+                                     nthreads or default_threads())
+    _check(st, "oracle_paged_decode")
+    return out, lse
+
+
+def paged_decode_partitioned(q, k_cache, v_cache, block_tables, context_lens, scale, part_tokens,
+                             nthreads=None):
+    """Partitioned paged decode merged by Eq. (4).
+
+    Returns dict(out, lse, part_m, part_l, part_o) in fp64.
+    """
+    qt, kt, vt, code, bt, cl, S, H, Hkv, D, BS, MB = _dec_args(q, k_cache, v_cache, block_tables,
+                                                               context_lens)
+    P = (MB * BS + part_tokens - 1) // part_tokens
+    out = np.empty((S, H, D), dtype=np.float64)
+    lse = np.empty((S, H), dtype=np.float64)
+    pm = np.empty((S, H, P), dtype=np.float64)
+    pl = np.empty((S, H, P), dtype=np.float64)
+    po = np.empty((S, H, P, D), dtype=np.float64)
+    st = _load().oracle_paged_decode_partitioned(
+        _p(qt), _p(kt), _p(vt), code, _p(bt), _p(cl), S, H, Hkv, D, BS, MB, float(scale),
+        int(part_tokens), _p(out), _p(lse), _p(pm), _p(pl), _p(po), nthreads or default_threads())
+    _check(st, "oracle_paged_decode_partitioned")
+    return dict(out=out, lse=lse, part_m=pm, part_l=pl, part_o=po)

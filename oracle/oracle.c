@@ -1,0 +1,657 @@
+/*
+ * oracle.c -- the exact-attention ORACLE: a plain, slow, obviously correct
+ * CPU implementation in fp64 of what the GPU path computes.
+ *
+ * THIS IS TEST INFRASTRUCTURE.  Only the test suite, the package's smoke
+ * check and the benchmark's CPU-baseline leg may load or call it.  The GPU
+ * library shares no code with it: no header, helper, table or constant
+ * generator is common to the two, and neither includes the other.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [SD]  "FlashAttention CUDA 커널 한 줄씩 살펴보기" (Korean translation of
+ *         Stephen Diehl's line-by-line FlashAttention kernel walkthrough,
+ *         yeokja.moreal.dev)
+ *   [SU]  "Flash Attention" (suniverse77.github.io), sections "Standard
+ *         Attention" and "Online Softmax", Eq. (1)-(4)
+ *   [FX]  "FlashAttention原理与CUDA实现" (fxlin0261.github.io), the
+ *         FlashAttention-2-order kernel listing
+ *   [YJ]  "FlashAttention: GPU 메모리 계층을 활용한 어텐션 최적화 분석"
+ *         (youngju.dev), sections 2.1, 5.1-5.2, 6.1-6.3, 7.2, 8.1-8.3, 11.3
+ *   [PA]  "PagedAttention" (data-sketchers.com wiki, vLLM kernel
+ *         walkthrough), sections "Concepts", "Key", "Softmax", "Value",
+ *         "Output"
+ *
+ * Conventions fixed here (the pages leave them open):
+ *   - Inputs are read from their storage type (fp32, bf16, fp16, fp64) and
+ *     widened exactly to fp64 by decoding the bit patterns from the IEEE 754
+ *     binary16 / bfloat16 definitions.
+ *   - Every sum runs in ascending index order; libm exp/log in fp64.
+ *   - lse is the natural log-sum-exp of the scaled, masked scores:
+ *     lse_i = m_i + ln(l_i).
+ *   - Causal mask: query row i sees keys j <= i (top-left aligned square
+ *     mask, the "is_causal" / lower-triangular mask of [YJ] 11.3).
+ *   - A row with no admissible key (cannot happen for the masks above) gets
+ *     O = 0 and lse = -inf.
+ *
+ * Build (no -ffast-math, so sums stay sequential and exp/log stay libm):
+ *   gcc -O2 -std=c11 -fPIC -shared -pthread oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_F64 = 3 };
+
+/* ------------------------------------------------------------------ */
+/* exact widening of storage types to fp64                              */
+/* ------------------------------------------------------------------ */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Normal: (1 + f/1024) * 2^(e-15); subnormal: f/1024 * 2^-14. */
+static double or_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24);
+    else if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + f), e - 25);
+    return sign ? -mag : mag;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32 bit pattern. */
+static double or_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double or_load(const void *base, int dtype, int64_t i)
+{
+    switch (dtype) {
+    case OR_F32: return (double)((const float *)base)[i];
+    case OR_BF16: return or_bf16_to_double(((const uint16_t *)base)[i]);
+    case OR_F16: return or_half_to_double(((const uint16_t *)base)[i]);
+    default: return ((const double *)base)[i];
+    }
+}
+
+static int or_elem_bytes(int dtype)
+{
+    switch (dtype) {
+    case OR_F32: return 4;
+    case OR_BF16: case OR_F16: return 2;
+    case OR_F64: return 8;
+    default: return 0;
+    }
+}
+
+/* Exported so that tests can pin the decoders against library conversions. */
+int oracle_widen(const void *src, int dtype, int64_t n, double *dst)
+{
+    if (or_elem_bytes(dtype) == 0) return -1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = or_load(src, dtype, i);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* thread pool helper: static partition of [0, n) over T threads        */
+/* ------------------------------------------------------------------ */
+
+typedef void (*or_item_fn)(void *ctx, int64_t item, double *scratch);
+
+typedef struct {
+    or_item_fn fn;
+    void *ctx;
+    int64_t begin, end;
+    int64_t scratch_len;
+    int status;
+} or_job;
+
+static void *or_run_job(void *arg)
+{
+    or_job *job = (or_job *)arg;
+    double *scratch = NULL;
+    if (job->scratch_len > 0) {
+        scratch = (double *)malloc((size_t)job->scratch_len * sizeof(double));
+        if (!scratch) { job->status = -1; return NULL; }
+    }
+    for (int64_t it = job->begin; it < job->end; ++it) job->fn(job->ctx, it, scratch);
+    free(scratch);
+    job->status = 0;
+    return NULL;
+}
+
+static int or_parallel(or_item_fn fn, void *ctx, int64_t n, int64_t scratch_len, int nthreads)
+{
+    if (n <= 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > n) nthreads = (int)n;
+    or_job jobs[256];
+    pthread_t tids[256];
+    int64_t chunk = (n + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].begin = (int64_t)t * chunk < n ? (int64_t)t * chunk : n;
+        jobs[t].end = (int64_t)(t + 1) * chunk < n ? (int64_t)(t + 1) * chunk : n;
+        jobs[t].scratch_len = scratch_len;
+        jobs[t].status = -1;
+    }
+    if (nthreads == 1) {
+        or_run_job(&jobs[0]);
+        return jobs[0].status;
+    }
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, or_run_job, &jobs[t]) != 0) break;
+        ++started;
+    }
+    for (int t = 0; t < started; ++t) pthread_join(tids[t], NULL);
+    if (started < nthreads) {
+        for (int t = started; t < nthreads; ++t) or_run_job(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (jobs[t].status != 0) return -1;
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* One softmax row, the plain definition                                */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Given n scores s[0..n) (already scaled and restricted to admissible keys),
+ * value rows v_of(j)[0..d) and output o[0..d):
+ *     m = max_j s_j,  p_j = exp(s_j - m),  l = sum_j p_j,
+ *     o_c = (sum_j p_j v_jc) / l,  return lse = m + ln l.
+ * This is the safe softmax of [SU] Eq. (1) ([YJ] 6.1, [PA] "Softmax")
+ * followed by O = PV ([SU] "Standard Attention", [YJ] 2.1).
+ * s is overwritten with p.
+ */
+typedef double (*or_value_fn)(const void *ctx, int64_t j, int c);
+
+static double or_softmax_row(double *s, int64_t n, int d, or_value_fn vfn, const void *vctx,
+                             double *o)
+{
+    if (n <= 0) {
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        return -INFINITY;
+    }
+    double m = s[0];
+    for (int64_t j = 1; j < n; ++j)
+        if (s[j] > m) m = s[j];
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < n; ++j) acc += s[j] * vfn(vctx, j, c);
+        o[c] = acc / l;
+    }
+    return m + log(l);
+}
+
+/* ------------------------------------------------------------------ */
+/* Dense attention forward                                              */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const void *q, *k, *v;
+    int dtype;
+    int B, H, N, d;
+    double scale;
+    int causal;
+    const int64_t *rows;
+    int64_t nrows;
+    double *o, *lse;
+    /* per-item value accessor context */
+} or_fwd_ctx;
+
+typedef struct {
+    const void *v;
+    int dtype;
+    int64_t base; /* element offset of V[b,h,0,0] */
+    int d;
+} or_dense_v;
+
+static double or_dense_value(const void *ctx, int64_t j, int c)
+{
+    const or_dense_v *dv = (const or_dense_v *)ctx;
+    return or_load(dv->v, dv->dtype, dv->base + j * dv->d + c);
+}
+
+static void or_fwd_item(void *vctx, int64_t item, double *s)
+{
+    const or_fwd_ctx *x = (const or_fwd_ctx *)vctx;
+    int64_t r = item % x->nrows;
+    int64_t bh = item / x->nrows;
+    int64_t i = x->rows ? x->rows[r] : r;
+    int64_t base = bh * (int64_t)x->N * x->d; /* [B,H,N,d] contiguous */
+    /* admissible keys A_i = { j < N : not causal or j <= i } */
+    int64_t n = x->causal ? (i + 1 < x->N ? i + 1 : x->N) : x->N;
+    for (int64_t j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int c = 0; c < x->d; ++c)
+            dot += or_load(x->q, x->dtype, base + i * x->d + c) *
+                   or_load(x->k, x->dtype, base + j * x->d + c);
+        s[j] = x->scale * dot;
+    }
+    or_dense_v dv = { x->v, x->dtype, base, x->d };
+    double *o = x->o + item * x->d;
+    x->lse[item] = or_softmax_row(s, n, x->d, or_dense_value, &dv, o);
+}
+
+/*
+ * O = softmax(scale * Q K^T [+ causal mask]) V for every (b, h) and every
+ * selected query row, with Q, K, V laid out [B, H, N, d] contiguous.
+ *   rows  : query indices to evaluate (the same for every (b, h)); NULL
+ *           means all N rows, in order.
+ *   o     : [B, H, nrows, d] fp64;  lse : [B, H, nrows] fp64.
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_attention(const void *q, const void *k, const void *v, int dtype, int B, int H, int N,
+                     int d, double scale, int causal, const int64_t *rows, int64_t nrows,
+                     double *o, double *lse, int nthreads)
+{
+    if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || N < 1 || d < 1) return -1;
+    if (or_elem_bytes(dtype) == 0) return -1;
+    if (!rows) nrows = N;
+    if (nrows < 1) return -1;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= N) return -1;
+    or_fwd_ctx ctx = { q, k, v, dtype, B, H, N, d, scale, causal, rows, nrows, o, lse };
+    return or_parallel(or_fwd_item, &ctx, (int64_t)B * H * nrows, N, nthreads);
+}
+
+/*
+ * The full probability matrix P = softmax(scale * Q K^T [+ mask]) for tiny
+ * inputs: P [B, H, N, N] fp64, masked entries exactly 0.
+ */
+int oracle_probs(const void *q, const void *k, int dtype, int B, int H, int N, int d, double scale,
+                 int causal, double *P)
+{
+    if (!q || !k || !P || B < 1 || H < 1 || N < 1 || d < 1) return -1;
+    if (or_elem_bytes(dtype) == 0) return -1;
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        int64_t base = bh * (int64_t)N * d;
+        for (int64_t i = 0; i < N; ++i) {
+            double *row = P + (bh * N + i) * N;
+            int64_t n = causal ? i + 1 : N;
+            for (int64_t j = 0; j < N; ++j) row[j] = 0.0;
+            if (n <= 0) continue;
+            for (int64_t j = 0; j < n; ++j) {
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c)
+                    dot += or_load(q, dtype, base + i * d + c) * or_load(k, dtype, base + j * d + c);
+                row[j] = scale * dot;
+            }
+            double m = row[0];
+            for (int64_t j = 1; j < n; ++j)
+                if (row[j] > m) m = row[j];
+            double l = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                row[j] = exp(row[j] - m);
+                l += row[j];
+            }
+            for (int64_t j = 0; j < n; ++j) row[j] /= l;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* The tiled online recurrence, in both loop orders (one head)          */
+/* ------------------------------------------------------------------ */
+
+/* score of query i against key j, -inf where the mask excludes it */
+static double or_score(const double *q, const double *k, int N, int d, double scale, int causal,
+                       int64_t i, int64_t j)
+{
+    if (j >= N || i >= N) return -INFINITY;
+    if (causal && j > i) return -INFINITY;
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c) dot += q[i * d + c] * k[j * d + c];
+    return scale * dot;
+}
+
+/*
+ * FlashAttention-1 loop order ([YJ] 5.2 pseudocode; [SD] "main loop"):
+ * outer loop over K/V tiles j, inner loop over Q tiles i; O, l, m live in
+ * "HBM" arrays (here: o, l, m) initialised to 0, 0, -inf and are read and
+ * written back on every (i, j) step.  Per step, with the tile's own
+ * statistics m~ = rowmax(S_ij), P~ = exp(S_ij - m~), l~ = rowsum(P~):
+ *     m_new = max(m, m~)
+ *     l_new = e^(m - m_new) l + e^(m~ - m_new) l~
+ *     O     = (l e^(m - m_new) O + e^(m~ - m_new) P~ V_j) / l_new
+ * The O update is the merge of two normalised partial results, [SU] Eq. (4);
+ * the printed pseudocode's inverse on the exponential factors is read as a
+ * typesetting slip, since Eq. (4) and [YJ] 6.2 carry no inverse.
+ * A tile row with no admissible key leaves that row's state unchanged.
+ * Outputs o [N, d] and lse [N] (lse = m + ln l).
+ */
+int oracle_tiled_fa1(const double *q, const double *k, const double *v, int N, int d, double scale,
+                     int causal, int Br, int Bc, double *o, double *lse)
+{
+    if (!q || !k || !v || !o || !lse || N < 1 || d < 1 || Br < 1 || Bc < 1) return -1;
+    double *m = (double *)malloc(sizeof(double) * N);
+    double *l = (double *)malloc(sizeof(double) * N);
+    double *pt = (double *)malloc(sizeof(double) * Bc);
+    if (!m || !l || !pt) { free(m); free(l); free(pt); return -1; }
+    for (int64_t i = 0; i < N; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.0;
+        for (int c = 0; c < d; ++c) o[i * d + c] = 0.0;
+    }
+    int Tr = (N + Br - 1) / Br, Tc = (N + Bc - 1) / Bc;
+    for (int j = 0; j < Tc; ++j) {
+        for (int it = 0; it < Tr; ++it) {
+            for (int r = 0; r < Br; ++r) {
+                int64_t i = (int64_t)it * Br + r;
+                if (i >= N) break;
+                double mt = -INFINITY;
+                for (int cc = 0; cc < Bc; ++cc) {
+                    pt[cc] = or_score(q, k, N, d, scale, causal, i, (int64_t)j * Bc + cc);
+                    if (pt[cc] > mt) mt = pt[cc];
+                }
+                if (mt == -INFINITY) continue; /* nothing admissible in this tile */
+                double lt = 0.0;
+                for (int cc = 0; cc < Bc; ++cc) {
+                    pt[cc] = exp(pt[cc] - mt); /* exp(-inf) = 0 for masked keys */
+                    lt += pt[cc];
+                }
+                double mnew = m[i] > mt ? m[i] : mt;
+                double a_old = exp(m[i] - mnew); /* 0 when m[i] = -inf */
+                double a_new = exp(mt - mnew);
+                double lnew = a_old * l[i] + a_new * lt;
+                for (int c = 0; c < d; ++c) {
+                    double pv = 0.0;
+                    for (int cc = 0; cc < Bc; ++cc) {
+                        int64_t jj = (int64_t)j * Bc + cc;
+                        if (jj < N) pv += pt[cc] * v[jj * d + c];
+                    }
+                    o[i * d + c] = (l[i] * a_old * o[i * d + c] + a_new * pv) / lnew;
+                }
+                m[i] = mnew;
+                l[i] = lnew;
+            }
+        }
+    }
+    for (int64_t i = 0; i < N; ++i) lse[i] = l[i] > 0.0 ? m[i] + log(l[i]) : -INFINITY;
+    free(m); free(l); free(pt);
+    return 0;
+}
+
+/*
+ * FlashAttention-2 loop order ([FX] kernel listing; [YJ] 8.1-8.2): outer
+ * loop over Q tiles, inner loop over K/V tiles, running (m, l) per row and an
+ * UNNORMALISED accumulator divided by l once at the end:
+ *     m_new = max(m, rowmax(S_ij))                  [SU] Eq. (2)
+ *     P~    = exp(S_ij - m_new)
+ *     l     = e^(m - m_new) l + rowsum(P~)          [SU] Eq. (3)
+ *     Oacc  = e^(m - m_new) Oacc + P~ V_j
+ *     O     = Oacc / l,  lse = m + ln l             (after the last tile)
+ */
+int oracle_tiled_fa2(const double *q, const double *k, const double *v, int N, int d, double scale,
+                     int causal, int Br, int Bc, double *o, double *lse)
+{
+    if (!q || !k || !v || !o || !lse || N < 1 || d < 1 || Br < 1 || Bc < 1) return -1;
+    double *pt = (double *)malloc(sizeof(double) * Bc);
+    if (!pt) return -1;
+    int Tr = (N + Br - 1) / Br, Tc = (N + Bc - 1) / Bc;
+    for (int it = 0; it < Tr; ++it) {
+        for (int r = 0; r < Br; ++r) {
+            int64_t i = (int64_t)it * Br + r;
+            if (i >= N) break;
+            double m = -INFINITY, l = 0.0;
+            double *acc = o + i * d;
+            for (int c = 0; c < d; ++c) acc[c] = 0.0;
+            for (int j = 0; j < Tc; ++j) {
+                double mt = -INFINITY;
+                for (int cc = 0; cc < Bc; ++cc) {
+                    pt[cc] = or_score(q, k, N, d, scale, causal, i, (int64_t)j * Bc + cc);
+                    if (pt[cc] > mt) mt = pt[cc];
+                }
+                double mnew = m > mt ? m : mt;
+                if (mnew == -INFINITY) continue; /* no admissible key seen yet */
+                double alpha = exp(m - mnew);
+                double rs = 0.0;
+                for (int cc = 0; cc < Bc; ++cc) {
+                    pt[cc] = exp(pt[cc] - mnew);
+                    rs += pt[cc];
+                }
+                l = alpha * l + rs;
+                for (int c = 0; c < d; ++c) {
+                    double pv = 0.0;
+                    for (int cc = 0; cc < Bc; ++cc) {
+                        int64_t jj = (int64_t)j * Bc + cc;
+                        if (jj < N) pv += pt[cc] * v[jj * d + c];
+                    }
+                    acc[c] = alpha * acc[c] + pv;
+                }
+                m = mnew;
+            }
+            if (l > 0.0) {
+                for (int c = 0; c < d; ++c) acc[c] /= l;
+                lse[i] = m + log(l);
+            } else {
+                lse[i] = -INFINITY;
+            }
+        }
+    }
+    free(pt);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Paged single-query decode                                            */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Cache layouts ([PA] "Inputs", "Concepts", "Key", "Value"):
+ *   k_cache [num_blocks, num_kv_heads, head_size/x, block_size, x]
+ *   v_cache [num_blocks, num_kv_heads, head_size, block_size]
+ * where x is the number of elements in one 16-byte vector (8 for fp16).
+ * Token t of sequence s lives in physical block block_tables[s][t / BS] at
+ * offset t % BS; query head h reads kv head h / (num_heads / num_kv_heads).
+ */
+typedef struct {
+    const void *q, *kc, *vc;
+    int dtype;
+    const int32_t *bt, *ctx_lens;
+    int S, H, Hkv, D, BS, MB, x;
+    double scale;
+    int part_tokens; /* 0: no partitioning */
+    double *out, *lse;
+    double *part_m, *part_l, *part_o; /* optional partition partials */
+    int P;                            /* partitions per (s, h) in part_* */
+} or_dec_ctx;
+
+static int64_t or_k_index(const or_dec_ctx *x, int64_t blk, int kvh, int e, int off)
+{
+    return ((((blk * x->Hkv + kvh) * (x->D / x->x) + e / x->x) * x->BS + off) * x->x) + e % x->x;
+}
+
+static int64_t or_v_index(const or_dec_ctx *x, int64_t blk, int kvh, int e, int off)
+{
+    return ((blk * x->Hkv + kvh) * (int64_t)x->D + e) * x->BS + off;
+}
+
+typedef struct {
+    const or_dec_ctx *x;
+    int s, kvh;
+    int64_t t0; /* first context token of the range */
+} or_paged_v;
+
+static double or_paged_value(const void *ctx, int64_t j, int e)
+{
+    const or_paged_v *pv = (const or_paged_v *)ctx;
+    const or_dec_ctx *x = pv->x;
+    int64_t t = pv->t0 + j;
+    int64_t blk = x->bt[(int64_t)pv->s * x->MB + t / x->BS];
+    return or_load(x->vc, x->dtype, or_v_index(x, blk, pv->kvh, e, (int)(t % x->BS)));
+}
+
+/* logits scale * q . K_t for t in [t0, t1) into s[0 .. t1-t0) */
+static void or_paged_logits(const or_dec_ctx *x, int s, int h, int64_t t0, int64_t t1, double *lg)
+{
+    int kvh = h / (x->H / x->Hkv);
+    int64_t qbase = ((int64_t)s * x->H + h) * x->D;
+    for (int64_t t = t0; t < t1; ++t) {
+        int64_t blk = x->bt[(int64_t)s * x->MB + t / x->BS];
+        int off = (int)(t % x->BS);
+        double dot = 0.0;
+        for (int e = 0; e < x->D; ++e)
+            dot += or_load(x->q, x->dtype, qbase + e) *
+                   or_load(x->kc, x->dtype, or_k_index(x, blk, kvh, e, off));
+        lg[t - t0] = x->scale * dot;
+    }
+}
+
+static void or_dec_item(void *vctx, int64_t item, double *scratch)
+{
+    const or_dec_ctx *x = (const or_dec_ctx *)vctx;
+    int s = (int)(item / x->H), h = (int)(item % x->H);
+    int kvh = h / (x->H / x->Hkv);
+    int64_t n = x->ctx_lens[s];
+    double *out = x->out + item * x->D;
+    if (x->part_tokens <= 0) {
+        or_paged_logits(x, s, h, 0, n, scratch);
+        or_paged_v pv = { x, s, kvh, 0 };
+        double l = or_softmax_row(scratch, n, x->D, or_paged_value, &pv, out);
+        if (x->lse) x->lse[item] = l;
+        return;
+    }
+    /*
+     * Partitioned form ([PA] grid axis max_num_partitions, "Softmax",
+     * "exp_sum", "Value", "Output"): each partition of part_tokens context
+     * tokens gets its own max m_p, exp-sum l_p and NORMALISED partial O_p;
+     * the partials are then merged with [SU] Eq. (4) generalised to P parts:
+     *     m = max_p m_p,  w_p = l_p e^(m_p - m),
+     *     O = sum_p w_p O_p / sum_p w_p,  lse = m + ln(sum_p w_p).
+     * An empty partition (m_p = -inf, l_p = 0) has weight 0.
+     */
+    double *op = scratch + x->part_tokens; /* D doubles for one partial */
+    int64_t nparts = (n + x->part_tokens - 1) / x->part_tokens;
+    double m_all = -INFINITY;
+    for (int64_t p = 0; p < nparts; ++p) {
+        double *pm = x->part_m + item * x->P + p;
+        double *pl = x->part_l + item * x->P + p;
+        int64_t t0 = p * x->part_tokens;
+        int64_t t1 = t0 + x->part_tokens < n ? t0 + x->part_tokens : n;
+        or_paged_logits(x, s, h, t0, t1, scratch);
+        double mp = scratch[0];
+        for (int64_t t = 1; t < t1 - t0; ++t)
+            if (scratch[t] > mp) mp = scratch[t];
+        double lp = 0.0;
+        for (int64_t t = 0; t < t1 - t0; ++t) {
+            scratch[t] = exp(scratch[t] - mp);
+            lp += scratch[t];
+        }
+        for (int64_t t = 0; t < t1 - t0; ++t) scratch[t] /= lp; /* normalised partition */
+        or_paged_v pv = { x, s, kvh, t0 };
+        for (int e = 0; e < x->D; ++e) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < t1 - t0; ++t) acc += scratch[t] * or_paged_value(&pv, t, e);
+            op[e] = acc;
+        }
+        *pm = mp;
+        *pl = lp;
+        for (int e = 0; e < x->D; ++e) x->part_o[(item * x->P + p) * x->D + e] = op[e];
+        if (mp > m_all) m_all = mp;
+    }
+    for (int64_t p = nparts; p < x->P; ++p) {
+        x->part_m[item * x->P + p] = -INFINITY;
+        x->part_l[item * x->P + p] = 0.0;
+        for (int e = 0; e < x->D; ++e) x->part_o[(item * x->P + p) * x->D + e] = 0.0;
+    }
+    double wsum = 0.0;
+    for (int e = 0; e < x->D; ++e) out[e] = 0.0;
+    for (int64_t p = 0; p < nparts; ++p) {
+        double w = x->part_l[item * x->P + p] * exp(x->part_m[item * x->P + p] - m_all);
+        wsum += w;
+        for (int e = 0; e < x->D; ++e) out[e] += w * x->part_o[(item * x->P + p) * x->D + e];
+    }
+    if (wsum > 0.0) {
+        for (int e = 0; e < x->D; ++e) out[e] /= wsum;
+        if (x->lse) x->lse[item] = m_all + log(wsum);
+    } else if (x->lse) {
+        x->lse[item] = -INFINITY;
+    }
+}
+
+static int or_dec_check(const void *q, const void *kc, const void *vc, int dtype,
+                        const int32_t *bt, const int32_t *cl, int S, int H, int Hkv, int D,
+                        int BS, int MB)
+{
+    if (!q || !kc || !vc || !bt || !cl) return -1;
+    int es = or_elem_bytes(dtype);
+    if (es == 0 || es > 16 || 16 % es) return -1;
+    if (S < 1 || H < 1 || Hkv < 1 || H % Hkv || D < 1 || BS < 1 || MB < 1) return -1;
+    if (D % (16 / es)) return -1;
+    for (int s = 0; s < S; ++s)
+        if (cl[s] < 0 || (int64_t)cl[s] > (int64_t)MB * BS) return -1;
+    return 0;
+}
+
+/*
+ * Single-query paged decode, unsplit: for every sequence s and head h,
+ * out[s,h,:] = softmax over t < context_lens[s] of scale * q[s,h] . K_t,
+ * applied to V_t (no causal mask).  out [S, H, D] fp64, lse [S, H] (may be
+ * NULL).  Context length 0 gives out = 0, lse = -inf.
+ */
+int oracle_paged_decode(const void *q, const void *k_cache, const void *v_cache, int dtype,
+                        const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                        int num_heads, int num_kv_heads, int head_size, int block_size,
+                        int max_blocks_per_seq, double scale, double *out, double *lse,
+                        int nthreads)
+{
+    if (or_dec_check(q, k_cache, v_cache, dtype, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_size, block_size, max_blocks_per_seq) || !out)
+        return -1;
+    or_dec_ctx x = { q, k_cache, v_cache, dtype, block_tables, context_lens,
+                     num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                     max_blocks_per_seq, 16 / or_elem_bytes(dtype), scale, 0,
+                     out, lse, NULL, NULL, NULL, 0 };
+    int64_t maxctx = (int64_t)max_blocks_per_seq * block_size;
+    return or_parallel(or_dec_item, &x, (int64_t)num_seqs * num_heads, maxctx, nthreads);
+}
+
+/*
+ * The same decode computed per context partition of part_tokens tokens and
+ * merged (see or_dec_item).  Also returns the partials:
+ *   part_m, part_l [S, H, P];  part_o [S, H, P, D]  with
+ *   P = ceil(max_blocks_per_seq * block_size / part_tokens).
+ */
+int oracle_paged_decode_partitioned(const void *q, const void *k_cache, const void *v_cache,
+                                    int dtype, const int32_t *block_tables,
+                                    const int32_t *context_lens, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_size, int block_size,
+                                    int max_blocks_per_seq, double scale, int part_tokens,
+                                    double *out, double *lse, double *part_m, double *part_l,
+                                    double *part_o, int nthreads)
+{
+    if (or_dec_check(q, k_cache, v_cache, dtype, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_size, block_size, max_blocks_per_seq) || !out)
+        return -1;
+    if (part_tokens < 1 || !part_m || !part_l || !part_o) return -1;
+    int64_t maxctx = (int64_t)max_blocks_per_seq * block_size;
+    int P = (int)((maxctx + part_tokens - 1) / part_tokens);
+    or_dec_ctx x = { q, k_cache, v_cache, dtype, block_tables, context_lens,
+                     num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                     max_blocks_per_seq, 16 / or_elem_bytes(dtype), scale, part_tokens,
+                     out, lse, part_m, part_l, part_o, P };
+    return or_parallel(or_dec_item, &x, (int64_t)num_seqs * num_heads,
+                       (int64_t)part_tokens + head_size, nthreads);
+}

@@ -1,0 +1,31 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (runs the HIP kernels)")
+
+
+@pytest.fixture(scope="session")
+def fa_lib():
+    """libfa.so loaded through the binding (built first only if absent)."""
+    import exact_attention_12_amd as fa
+    if not os.path.exists(fa.lib_path()):
+        from exact_attention_12_amd import build
+        build.build()
+    return fa.load_library()
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    """The HIP device; a GPU test without one fails loudly instead of skipping."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    return torch.device("cuda:0")
