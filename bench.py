@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. fa_fwd on the headline forward workload: B=2, H=32, N=8192, d=128, bf16,
+     causal, scale 1/sqrt(128), Q/K/V iid N(0,1);
+  2. fa_paged_decode on the decode workload: 64 sequences x 32 heads, head
+     size 128, fp16, block size 16, context lengths uniform in [512, 4096],
+     a 20000-block pool addressed through a random permutation.
+Inputs are generated on the host with fixed seeds and copied to HBM before
+the timed region.  The timed region runs K steps between two device
+synchronisations; each kernel call is bracketed by HIP events recorded on the
+stream the kernels run on (torch's current stream).
+
+Prints ONE JSON line.  `value` is the forward pass's throughput in TFLOP/s
+(4*B*H*N^2*d / 2 for causal, per second of fa_fwd time); the decode's HBM
+bandwidth (algorithmic bytes per second of fa_paged_decode time) is reported
+under "decode".  `cpu_baseline` times the fp64 CPU oracle on a bounded sample
+of the forward workload (one head, evenly spaced query rows).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak (published)
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_attention_12_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they are current."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, scale, causal, target_s=12.0):
+    """Time the oracle on head (0, 0) of the forward workload, rows evenly spaced."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    qh, kh, vh = (t[:1, :1].contiguous() for t in (q, k, v))
+    N, d = qh.shape[2], qh.shape[3]
+
+    def run(R):
+        rows = np.unique(np.linspace(0, N - 1, R).round().astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.attention(qh, kh, vh, scale, causal, rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        keys = (rows + 1).sum() if causal else len(rows) * N
+        return dt, 4.0 * d * float(keys), len(rows)
+
+    dt, fl, R = run(64)
+    R2 = int(min(N, max(64, 64 * target_s / max(dt, 1e-3))))
+    if R2 > 64:
+        dt, fl, R = run(R2)
+    return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                seconds=round(dt, 3),
+                sample="fp64 oracle on head (0,0) of the forward workload: %d query rows evenly "
+                       "spaced over N=%d, causal, %.3g flop" % (R, N, fl))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle timing (e.g. under a profiler)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_12_amd as fa
+    from exact_attention_12_amd import inputs
+
+    if not os.path.exists(fa.lib_path()):
+        from exact_attention_12_amd import build as fa_build
+        fa_build.build()
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- inputs (host, seeded) -> HBM
+    fcfg = inputs.FWD_CONFIGS[3]
+    log("generating forward inputs: " + fcfg.name)
+    q, k, v = inputs.fwd_inputs(fcfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    B, H, N, d = qd.shape
+    fscale = float(np.float32(fcfg.scale))
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    dcfg = inputs.DECODE_CONFIG
+    log("generating decode inputs: " + dcfg.name)
+    dec = inputs.decode_inputs(dcfg)
+    dq, dk, dv = dec["q"].to(dev), dec["k_cache"].to(dev), dec["v_cache"].to(dev)
+    dbt, dcl = dec["block_tables"].to(dev), dec["context_lens"].to(dev)
+    maxctx = dec["max_context_len"]
+    S, Hq, D = dq.shape
+    Hkv, BS = dk.shape[1], dk.shape[3]
+    MB = dbt.shape[1]
+    dscale = float(np.float32(dcfg.scale))
+    dout = torch.empty_like(dq)
+    ws_bytes = fa.fa_paged_decode_workspace_size(S, Hq, D, maxctx)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    del dec["k_cache"], dec["v_cache"]
+
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        fa.fa_fwd(qd, kd, vd, o, lse, B, H, N, d, fscale, True, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        fa.fa_paged_decode(dq, dk, dv, dbt, dcl, dout, S, Hq, Hkv, D, BS, MB, maxctx, dscale, ws,
+                           stream=stream)
+        if evs:
+            evs[2].record(stream)
+
+    log("warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    # quick sanity of the last step's results (full parity lives in the tests)
+    finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item())
+
+    flops = fcfg.flops()
+    tflops = flops / (fwd_avg * 1e-3) / 1e12
+    ctx = dec["context_lens"].numpy().astype(np.int64)
+    esz = dq.element_size()
+    dec_bytes = (int(ctx.sum()) * Hkv * D * esz * 2          # K and V of every context token
+                 + S * Hq * D * esz * 2                      # q read, out written
+                 + int(((ctx + BS - 1) // BS).sum()) * 4 + S * 4)  # table entries, lengths
+    dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+
+    fwd_hash = source_hash("fa_fwd.hip", "fa_device.h")
+    dec_hash = source_hash("fa_decode.hip", "fa_device.h")
+    fwd_traffic = measured_traffic("fa_fwd_kernel", fwd_hash)
+    dec_traffic = measured_traffic("fa_decode_partition_kernel", dec_hash)
+
+    result = {
+        "metric": "attn fwd TFLOP/s + % bf16 MFMA peak (N=8192,d=128,causal); decode HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "attention forward B=2 H=32 N=8192 d=128 bf16 causal (fp32 O, lse) "
+                        "+ paged decode 64 seqs x 32 heads x 128, fp16, block 16, "
+                        "ctx U[512,4096], 20000-block pool",
+            "fwd": {"B": B, "H": H, "N": N, "d": d, "causal": True, "flop": flops,
+                    "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(min(fwd_ms), 4),
+                    "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2)},
+            "decode": {"num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D,
+                       "block_size": BS, "sum_ctx": int(ctx.sum()), "max_ctx": maxctx,
+                       "algorithmic_bytes": dec_bytes, "ms_avg": round(dec_avg, 4),
+                       "ms_min": round(min(dec_ms), 4)},
+            "outputs_finite": finite,
+        },
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": fwd_traffic, "kernel": "fa_fwd_kernel<bf16,128,causal>",
+                     "algorithmic_per_launch": flops},
+        "decode": {"metric": "paged decode HBM bandwidth", "value": round(dec_gbs, 1),
+                   "unit": "GB/s",
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": dec_traffic,
+                                "kernel": "fa_decode_partition_kernel + fa_decode_merge_kernel",
+                                "algorithmic_per_launch": dec_bytes}},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(q, k, v, fscale, True)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

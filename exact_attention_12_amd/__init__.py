@@ -1,0 +1,187 @@
+"""exact_attention_12_amd -- exact attention on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libfa.so`` (C ABI in ``include/fa.h``).  The
+functions named like the C entry points (``fa_fwd``, ``fa_paged_decode``,
+``fa_paged_decode_workspace_size``, ``fa_strerror``) only marshal arguments:
+every step of the computation runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams.  ``forward`` and ``paged_decode`` are
+conveniences that allocate the outputs and call those entry points.
+
+There is no fallback: if ``libfa.so`` is missing or fails to load, every call
+raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "FA_F32", "FA_BF16", "FA_F16", "FA_DECODE_PARTITION_TOKENS", "FAError",
+    "fa_fwd", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror",
+    "forward", "paged_decode", "lib_path", "load_library",
+]
+
+FA_F32, FA_BF16, FA_F16 = 0, 1, 2
+FA_DECODE_PARTITION_TOKENS = 256  # must match include/fa.h
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_DTYPE_CODE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
+
+
+class FAError(RuntimeError):
+    """A non-zero status returned by libfa.so."""
+
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, fa_strerror(status), status))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+def load_library():
+    """Load libfa.so once; raise if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libfa.so is not built (expected at %s); build it with "
+            "`python -m exact_attention_12_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_paged_decode_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_paged_decode_workspace_size.restype = sz
+    lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_paged_decode.restype = i
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(dtype):
+    try:
+        return _DTYPE_CODE[dtype]
+    except KeyError:
+        raise TypeError("unsupported element type %s" % dtype) from None
+
+
+def fa_strerror(status: int) -> str:
+    return load_library().fa_strerror(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype=None, stream=None):
+    """C entry point ``fa_fwd``: enqueue the forward pass on ``stream``.
+
+    q, k, v: [B, H, N, d] device tensors (or raw device addresses) of one
+    element type; o: [B, H, N, d] fp32; lse: [B, H, N] fp32.  ``dtype``
+    defaults to q's element type.
+    """
+    if dtype is None:
+        dtype = _dtype_code(q.dtype)
+    st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                               int(N), int(d), float(scale), int(bool(causal)), int(dtype),
+                               _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_fwd")
+
+
+def fa_paged_decode_workspace_size(num_seqs, num_heads, head_size, max_context_len) -> int:
+    """C entry point ``fa_paged_decode_workspace_size`` (bytes; 0 if invalid)."""
+    return int(load_library().fa_paged_decode_workspace_size(
+        int(num_seqs), int(num_heads), int(head_size), int(max_context_len)))
+
+
+def fa_paged_decode(q, k_cache, v_cache, block_tables, context_lens, out, num_seqs, num_heads,
+                    num_kv_heads, head_size, block_size, max_blocks_per_seq, max_context_len,
+                    scale, workspace, workspace_bytes=None, dtype=None, stream=None):
+    """C entry point ``fa_paged_decode``: enqueue the paged decode on ``stream``."""
+    if dtype is None:
+        dtype = _dtype_code(q.dtype)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().fa_paged_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(out),
+        int(num_seqs), int(num_heads), int(num_kv_heads), int(head_size), int(block_size),
+        int(max_blocks_per_seq), int(max_context_len), float(scale), int(dtype),
+        _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_paged_decode")
+
+
+def _check_dev(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """Allocate o (fp32) and lse (fp32) and run ``fa_fwd``; returns (o, lse)."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_dev("out", out, torch.float32)
+    _check_dev("lse", lse, torch.float32)
+    fa_fwd(q, k, v, out, lse, B, H, N, d, scale, causal, stream=stream)
+    return out, lse
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
+                 out=None, workspace=None, stream=None):
+    """Allocate out and the workspace and run ``fa_paged_decode``; returns out."""
+    _check_dev("q", q)
+    _check_dev("k_cache", k_cache, q.dtype)
+    _check_dev("v_cache", v_cache, q.dtype)
+    _check_dev("block_tables", block_tables, torch.int32)
+    _check_dev("context_lens", context_lens, torch.int32)
+    S, H, D = q.shape
+    num_kv_heads = k_cache.shape[1]
+    block_size = k_cache.shape[3]
+    mbs = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = fa_paged_decode_workspace_size(S, H, D, max_context_len)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    fa_paged_decode(q, k_cache, v_cache, block_tables, context_lens, out, S, H, num_kv_heads, D,
+                    block_size, mbs, max_context_len, scale, workspace, stream=stream)
+    return out

@@ -1,0 +1,128 @@
+// fa_capi.cpp -- the C ABI of libfa.so (declared in include/fa.h): host-side
+// validation of every argument, then dispatch to the gfx950 kernels.
+// Validation runs before any HIP call, so an invalid call launches nothing
+// and writes nothing.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+namespace fa {
+hipError_t fwd_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
+                        int H, int N, int d, float scale, int causal, int dtype,
+                        hipStream_t stream);
+hipError_t decode_dispatch(const void *q, const void *kc, const void *vc, const int32_t *bt,
+                           const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
+                           int max_ctx, float scale, int dtype, void *workspace,
+                           hipStream_t stream);
+size_t decode_workspace_bytes(int num_seqs, int num_heads, int max_context_len);
+}  // namespace fa
+
+namespace {
+
+constexpr int kFwdRowsPerWorkgroup = 128;
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elem_bytes(int dtype)
+{
+    switch (dtype) {
+    case FA_F32: return 4;
+    case FA_BF16:
+    case FA_F16: return 2;
+    default: return 0;
+    }
+}
+
+// [a, a + na) and [b, b + nb) share a byte
+bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+bool valid_scale(float s) { return std::isfinite(s) && s >= 0.f; }
+
+}  // namespace
+
+extern "C" int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B,
+                      int H, int N, int d, float scale, int causal, int dtype, void *stream)
+{
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+    const int es = elem_bytes(dtype);
+    if (es == 0) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const int64_t qtiles = ((int64_t)N + kFwdRowsPerWorkgroup - 1) / kFwdRowsPerWorkgroup;
+    if ((int64_t)B * H * qtiles > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4))
+        return FA_ERR_ALIGNMENT;
+    const uint64_t rows = (uint64_t)B * H * N;
+    const uint64_t in_bytes = rows * d * es, o_bytes = rows * d * 4, l_bytes = rows * 4;
+    if (overlap(o, o_bytes, lse, l_bytes)) return FA_ERR_INVALID_ARG;
+    for (const void *in : {q, k, v})
+        if (overlap(o, o_bytes, in, in_bytes) || overlap(lse, l_bytes, in, in_bytes))
+            return FA_ERR_INVALID_ARG;
+    const hipError_t e = fa::fwd_dispatch(q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0,
+                                          dtype, (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" size_t fa_paged_decode_workspace_size(int num_seqs, int num_heads, int head_size,
+                                                 int max_context_len)
+{
+    if (num_seqs < 1 || num_heads < 1 || head_size != 128 || max_context_len < 0) return 0;
+    return fa::decode_workspace_bytes(num_seqs, num_heads, max_context_len);
+}
+
+extern "C" int fa_paged_decode(const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               void *out, int num_seqs, int num_heads, int num_kv_heads,
+                               int head_size, int block_size, int max_blocks_per_seq,
+                               int max_context_len, float scale, int dtype, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+        return FA_ERR_INVALID_ARG;
+    if (num_seqs < 1 || num_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
+        max_blocks_per_seq < 1 || max_context_len < 0)
+        return FA_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return FA_ERR_INVALID_ARG;
+    if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return FA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+    if (elem_bytes(dtype) == 0) return FA_ERR_INVALID_ARG;
+    if (dtype == FA_F32 || head_size != 128 || block_size != 16) return FA_ERR_UNSUPPORTED;
+    const int64_t nparts =
+        ((int64_t)max_context_len + FA_DECODE_PARTITION_TOKENS - 1) / FA_DECODE_PARTITION_TOKENS;
+    if (num_seqs > kMaxGridYZ || nparts > kMaxGridYZ) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return FA_ERR_ALIGNMENT;
+    const size_t need = fa::decode_workspace_bytes(num_seqs, num_heads, max_context_len);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return FA_ERR_ALIGNMENT;
+    const hipError_t e = fa::decode_dispatch(q, k_cache, v_cache, block_tables, context_lens, out,
+                                             num_seqs, num_heads, num_kv_heads, max_blocks_per_seq,
+                                             max_context_len, scale, dtype, workspace,
+                                             (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" const char *fa_strerror(int status)
+{
+    switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_ALIGNMENT: return "misaligned pointer";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}

@@ -1,0 +1,275 @@
+// fa_decode.hip -- single-query attention over a paged KV cache, gfx950.
+//
+// Structure follows "PagedAttention" (data-sketchers.com wiki): one
+// workgroup per (head, sequence, context partition); the query is held by
+// every lane; each wave walks a share of the partition's cache blocks, forms
+// q.k for the 16 tokens of a block with 16-byte vector loads and a cross-lane
+// reduction (section "QK"); the logits go to LDS; a workgroup-wide max and
+// exp-sum follow (sections "qk_max and logits", "exp_sum"); the values are
+// accumulated per head element (sections "Value", "LV") and the partition's
+// normalised partial result is written out (section "Output").  A second
+// kernel merges the partitions with Eq. (4) of "Flash Attention"
+// (suniverse77.github.io), generalised to P parts:
+//     m = max_p m_p,  w_p = l_p e^(m_p - m),  out = sum_p w_p O_p / sum_p w_p.
+//
+// The lane map is this library's own, for 64-wide waves:
+//  K block (16 tokens, [head/8][16][8] elements, 4 KiB contiguous): lane l
+//    loads the 16-byte vectors l, l+64, l+128, l+192, i.e. token l % 16 and
+//    head groups l/16 + 4c (c = 0..3); the 4 lanes of a token combine their
+//    partial dots with two cross-lane exchanges.
+//  V block ([head][16] elements, 4 KiB contiguous): lane l loads vectors
+//    l + 64c, i.e. head element l/2 + 32c and tokens 8*(l%2) .. +7; partial
+//    sums combine across the lane pair and then across waves through LDS.
+#include "fa.h"
+#include "fa_device.h"
+
+namespace fa {
+
+constexpr int kDecD = 128;        // head size
+constexpr int kDecBS = 16;        // tokens per cache block
+constexpr int kDecPart = FA_DECODE_PARTITION_TOKENS;  // context tokens per partition
+constexpr int kDecBlk = kDecPart / kDecBS;  // cache blocks per partition (16)
+constexpr int kDecThreads = 256;  // 4 waves
+constexpr int kDecWaves = kDecThreads / kWave;
+constexpr int kDecBPW = kDecBlk / kDecWaves;  // blocks per wave (4)
+
+template <typename T> __device__ __forceinline__ float elem_to_f32(uint32_t bits16);
+template <> __device__ __forceinline__ float elem_to_f32<_Float16>(uint32_t b)
+{
+    _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)b);
+    return (float)x;
+}
+template <> __device__ __forceinline__ float elem_to_f32<__bf16>(uint32_t b)
+{
+    return __builtin_bit_cast(float, b << 16);
+}
+
+// element e (0..7) of a 16-byte vector of 16-bit values, widened exactly
+template <typename T> __device__ __forceinline__ float vec_elem(const u32x4 &v, int e)
+{
+    return elem_to_f32<T>((v[e / 2] >> (16 * (e % 2))) & 0xffffu);
+}
+
+struct DecWs {
+    float *o;  // [S, H, P, D]
+    float *m;  // [S, H, P]
+    float *l;  // [S, H, P]
+};
+
+template <typename T>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ kc,
+                                const T *__restrict__ vc, const int32_t *__restrict__ block_tables,
+                                const int32_t *__restrict__ context_lens, int num_heads,
+                                int num_kv_heads, int max_blocks_per_seq, int nparts,
+                                float scale, DecWs ws)
+{
+    const int h = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int ctx = context_lens[s];
+    const int t0 = p * kDecPart;
+    const int64_t pidx = ((int64_t)s * num_heads + h) * nparts + p;
+    if (t0 >= ctx) {
+        // empty partition: weight 0 in the merge
+        if (tid == 0) {
+            ws.m[pidx] = -INFINITY;
+            ws.l[pidx] = 0.f;
+        }
+        return;
+    }
+    const int ntok = min(kDecPart, ctx - t0);
+    const int nblk = (ntok + kDecBS - 1) / kDecBS;
+    const int kvh = h / (num_heads / num_kv_heads);
+
+    __shared__ int tbl[kDecBlk];
+    __shared__ __attribute__((aligned(16))) float logits[kDecPart];
+    __shared__ float red[2][kDecWaves];
+    __shared__ float part[kDecWaves][kDecD];
+
+    if (tid < nblk) tbl[tid] = block_tables[(int64_t)s * max_blocks_per_seq + t0 / kDecBS + tid];
+
+    // q elements this lane dots with: head groups g = lane/16 + 4c.
+    float qv[4][8];
+    {
+        const T *qp = q + ((int64_t)s * num_heads + h) * kDecD;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 v = *(const u32x4 *)(qp + (lane / 16 + 4 * c) * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[c][e] = vec_elem<T>(v, e);
+        }
+    }
+    __syncthreads();
+
+    // Issue every K and V load of this wave's blocks up front.
+    u32x4 kr[kDecBPW][4], vr[kDecBPW][4];
+#pragma unroll
+    for (int i = 0; i < kDecBPW; ++i) {
+        const int b = wave + kDecWaves * i;
+        if (b < nblk) {
+            const int64_t base = ((int64_t)tbl[b] * num_kv_heads + kvh) * (kDecD * kDecBS);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                kr[i][c] = *(const u32x4 *)(kc + base + (lane + 64 * c) * 8);
+                vr[i][c] = *(const u32x4 *)(vc + base + (lane + 64 * c) * 8);
+            }
+        }
+    }
+
+    // logits = scale * q . k for the tokens of each block
+    float wmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kDecBPW; ++i) {
+        const int b = wave + kDecWaves * i;
+        if (b < nblk) {
+            float dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[c][e], vec_elem<T>(kr[i][c], e), dot);
+            dot += __shfl_xor(dot, 16, kWave);
+            dot += __shfl_xor(dot, 32, kWave);
+            const int tok = t0 + b * kDecBS + lane % 16;
+            const float lg = (tok < ctx) ? scale * dot : -INFINITY;
+            if (lane < 16) logits[b * kDecBS + lane] = lg;
+            wmax = fmaxf(wmax, lg);
+        }
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off /= 2) wmax = fmaxf(wmax, __shfl_xor(wmax, off, kWave));
+    if (lane == 0) red[0][wave] = wmax;
+    __syncthreads();
+    float m_p = red[0][0];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) m_p = fmaxf(m_p, red[0][w]);
+
+    // p_t = exp(logit_t - m_p); l_p = sum_t p_t  (one token per thread)
+    float pt = 0.f;
+    if (tid < nblk * kDecBS) {
+        pt = exp2_hw((logits[tid] - m_p) * kLog2e);  // masked: exp2(-inf) = 0
+        logits[tid] = pt;
+    }
+    float ps = pt;
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) ps += __shfl_xor(ps, off, kWave);
+    if (lane == 0) red[1][wave] = ps;
+    __syncthreads();
+    float l_p = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) l_p += red[1][w];
+
+    // acc[c] = sum_t p_t V_t[e] for e = lane/2 + 32c over this lane's tokens
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kDecBPW; ++i) {
+        const int b = wave + kDecWaves * i;
+        if (b < nblk) {
+            const int tb = b * kDecBS + 8 * (lane % 2);  // partition-relative first token
+            const f32x4 pa = *(const f32x4 *)(logits + tb);
+            const f32x4 pb = *(const f32x4 *)(logits + tb + 4);
+            const float pw[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+            const int nvalid = ntok - tb;  // tokens >= ntok are outside the context
+            if (nvalid >= 8) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[c] = __builtin_fmaf(pw[e], vec_elem<T>(vr[i][c], e), acc[c]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (e < nvalid) acc[c] = __builtin_fmaf(pw[e], vec_elem<T>(vr[i][c], e), acc[c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        acc[c] += __shfl_xor(acc[c], 1, kWave);
+        if (lane % 2 == 0) part[wave][lane / 2 + 32 * c] = acc[c];
+    }
+    __syncthreads();
+    if (tid < kDecD) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) o += part[w][tid];
+        ws.o[pidx * kDecD + tid] = o / l_p;  // normalised partial ("exp_sum": logits * inv_sum)
+    }
+    if (tid == 0) {
+        ws.m[pidx] = m_p;
+        ws.l[pidx] = l_p;
+    }
+}
+
+template <typename T> __device__ __forceinline__ T f32_to_elem(float x) { return (T)x; }
+
+template <typename T>
+__global__ __attribute__((amdgpu_flat_work_group_size(128, 128)))
+void fa_decode_merge_kernel(const int32_t *__restrict__ context_lens, T *__restrict__ out,
+                            int num_heads, int nparts, DecWs ws)
+{
+    const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+    const int ctx = context_lens[s];
+    const int np = min(nparts, (ctx + kDecPart - 1) / kDecPart);
+    const int64_t row = (int64_t)s * num_heads + h;
+    const int64_t base = row * nparts;
+    float m = -INFINITY;
+    for (int p = 0; p < np; ++p) m = fmaxf(m, ws.m[base + p]);
+    float wsum = 0.f, o = 0.f;
+    for (int p = 0; p < np; ++p) {
+        const float w = ws.l[base + p] * exp2_hw((ws.m[base + p] - m) * kLog2e);
+        wsum += w;
+        o = __builtin_fmaf(w, ws.o[(base + p) * kDecD + d], o);
+    }
+    out[row * kDecD + d] = f32_to_elem<T>(np > 0 ? o / wsum : 0.f);
+}
+
+size_t decode_workspace_bytes(int num_seqs, int num_heads, int max_context_len)
+{
+    const int64_t np = (max_context_len + kDecPart - 1) / kDecPart;
+    const int64_t parts = (int64_t)num_seqs * num_heads * (np > 0 ? np : 1);
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    return (size_t)(up(parts * kDecD * 4) + 2 * up(parts * 4));
+}
+
+template <typename T>
+static hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int32_t *bt,
+                                const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
+                                int max_ctx, float scale, void *workspace, hipStream_t stream)
+{
+    const int np = (max_ctx + kDecPart - 1) / kDecPart;
+    if (np == 0) {
+        // every context is empty: the merge writes zeros
+        DecWs ws{(float *)workspace, (float *)workspace, (float *)workspace};
+        hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3(H, S), dim3(kDecD), 0, stream, cl,
+                           (T *)out, H, 0, ws);
+        return hipGetLastError();
+    }
+    const int64_t parts = (int64_t)S * H * np;
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    char *w = (char *)workspace;
+    DecWs ws{(float *)w, (float *)(w + up(parts * kDecD * 4)),
+             (float *)(w + up(parts * kDecD * 4) + up(parts * 4))};
+    hipLaunchKernelGGL(fa_decode_partition_kernel<T>, dim3(H, S, np), dim3(kDecThreads), 0, stream,
+                       (const T *)q, (const T *)kc, (const T *)vc, bt, cl, H, Hkv, MB, np, scale,
+                       ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3(H, S), dim3(kDecD), 0, stream, cl, (T *)out,
+                       H, np, ws);
+    return hipGetLastError();
+}
+
+hipError_t decode_dispatch(const void *q, const void *kc, const void *vc, const int32_t *bt,
+                           const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
+                           int max_ctx, float scale, int dtype, void *workspace,
+                           hipStream_t stream)
+{
+    if (dtype == 2)
+        return launch_decode<_Float16>(q, kc, vc, bt, cl, out, S, H, Hkv, MB, max_ctx, scale,
+                                       workspace, stream);
+    return launch_decode<__bf16>(q, kc, vc, bt, cl, out, S, H, Hkv, MB, max_ctx, scale, workspace,
+                                 stream);
+}
+
+}  // namespace fa

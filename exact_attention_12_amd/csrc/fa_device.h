@@ -1,0 +1,90 @@
+// fa_device.h -- device-side building blocks for gfx950 (CDNA4): vector
+// types, the matrix-core (MFMA) operand traits per element type, and small
+// wave-level helpers.  Included only by the .hip sources of libfa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// log2(e): exp(x) = 2^(x * log2 e); the hardware exponential is base 2.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x on the hardware transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the hardware transcendental unit (v_log_f32).
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------------------
+// Matrix-core traits.  One 32x32 output tile per instruction; the contraction
+// depth per instruction is 2*KW, and every lane supplies KW consecutive
+// k-elements of one A row / one B column:
+//   A (32 x 2KW): lane l holds A[l % 32][KW*(l/32) .. KW*(l/32)+KW-1]
+//   B (2KW x 32): lane l holds B[KW*(l/32) .. +KW-1][l % 32]
+//   C (32 x 32) : lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l % 32]
+// 16-bit types use v_mfma_f32_32x32x16_{bf16,f16} (KW = 8, one 16-byte
+// fragment per lane); fp32 uses v_mfma_f32_32x32x2_f32 (KW = 1).
+// ---------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<__bf16> {
+    static constexpr int KW = 8;
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    // 8 fp32 -> 8 bf16, round to nearest even (v_cvt_pk_bf16_f32)
+    static __device__ __forceinline__ frag pack(const float *x)
+    {
+        frag r;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+        return r;
+    }
+};
+
+template <> struct Mma<_Float16> {
+    static constexpr int KW = 8;
+    typedef f16x8 frag;
+    static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag pack(const float *x)
+    {
+        frag r;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];
+        return r;
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int KW = 1;
+    typedef float frag;
+    static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag pack(const float *x) { return x[0]; }
+};
+
+// Row (within a 32-row tile) held by lane-half h in accumulator register r.
+__device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r / 4) + 4 * h + r % 4; }
+
+// Cross-half exchange: value held by lane l ^ 32.
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, kWave); }
+
+}  // namespace fa

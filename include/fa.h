@@ -1,0 +1,142 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact attention for AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, both exact (no approximation of softmax):
+ *
+ *  1. fa_fwd: the FlashAttention forward pass, O = softmax(scale * Q K^T
+ *     [+ causal mask]) V for every (batch, head), computed tile by tile with
+ *     the online-softmax running max m and running sum l so that the N x N
+ *     score matrix never reaches HBM.  Defined by "FlashAttention: GPU 메모리
+ *     계층을 활용한 어텐션 최적화 분석" (youngju.dev), sections 2.1 (standard
+ *     attention), 5.1-5.2 (tiling), 6.2 (online softmax) and 8.1-8.3
+ *     (FlashAttention-2 order); "Flash Attention" (suniverse77.github.io),
+ *     Eq. (1)-(4).
+ *
+ *  2. fa_paged_decode: single-query attention of one new token per sequence
+ *     against its context stored in a paged (block-table) KV cache, split
+ *     into context partitions whose partial results (m, l, O) are merged with
+ *     Eq. (4) of "Flash Attention" generalised to P parts.  The cache layout
+ *     and the decode structure are those of "PagedAttention"
+ *     (data-sketchers.com wiki), sections "Inputs", "Concepts", "Key",
+ *     "Softmax", "Value", "Output".
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE memory owned by the caller; the library
+ *    allocates nothing and keeps no pointer after the call returns.
+ *  - Calls enqueue work on `stream` (a hipStream_t passed as void*, NULL for
+ *    the default stream) and return at once; results are ready after the
+ *    caller synchronises that stream.
+ *  - Arguments are validated on the host before anything is launched.  On a
+ *    non-zero status nothing was launched and nothing was written.  A launch
+ *    failure reported by the HIP runtime returns FA_ERR_HIP.  Device faults
+ *    surface at the caller's next synchronisation.
+ *  - Thread-safe.  Deterministic: identical inputs give bitwise identical
+ *    outputs (fixed reduction order, no atomics).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of q, k, v (fa_fwd) and of q, caches, out (fa_paged_decode) */
+typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype_t;
+
+/* status codes */
+enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad scale ...   */
+    FA_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head dim 96)     */
+    FA_ERR_ALIGNMENT = -3,   /* a pointer is not aligned as documented           */
+    FA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required       */
+    FA_ERR_HIP = -5          /* the HIP runtime refused a launch                 */
+};
+
+/*
+ * fa_fwd -- exact attention forward.
+ *
+ *   q, k, v : [B, H, N, d] contiguous (d fastest), element type `dtype`,
+ *             16-byte aligned.  Read only.
+ *   o       : [B, H, N, d] contiguous fp32, 16-byte aligned.  Written:
+ *             o[b,h,i,:] = sum_j P_ij v[b,h,j,:] with
+ *             P_ij = exp(s_ij - m_i) / l_i,  s_ij = scale * q_i . k_j,
+ *             m_i = max_j s_ij, l_i = sum_j exp(s_ij - m_i), over the keys j
+ *             that row i may see.
+ *   lse     : [B, H, N] fp32, 4-byte aligned.  Written: lse_i = m_i + ln l_i
+ *             (natural log of sum_j exp(s_ij)), the per-row statistic kept
+ *             for a recomputing backward pass (youngju.dev section 7.2).
+ *   B, H, N : batch, heads, sequence length, each >= 1.
+ *   d       : head dimension, 64 or 128 (else FA_ERR_UNSUPPORTED).
+ *   scale   : finite and >= 0 (usually 1/sqrt(d)); else FA_ERR_INVALID_ARG.
+ *   causal  : non-zero: row i sees keys j <= i only (top-left aligned square
+ *             mask, youngju.dev section 11.3); zero: all N keys.
+ *   dtype   : FA_F32, FA_BF16 or FA_F16.  Products are exact and accumulate
+ *             in fp32; the softmax probabilities are rounded (round to
+ *             nearest even) to `dtype` before the P.V product on the matrix
+ *             cores (kept in fp32 for FA_F32).
+ *   stream  : hipStream_t or NULL.
+ * q/k/v may alias each other; o and lse must not overlap any input.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int N,
+           int d, float scale, int causal, int dtype, void *stream);
+
+/*
+ * fa_paged_decode_workspace_size -- bytes of device workspace that
+ * fa_paged_decode needs for these sizes: the per-partition partial results
+ * O_p [S, H, P, head_size] fp32 plus m_p and l_p [S, H, P] fp32, where
+ * P = ceil(max_context_len / FA_DECODE_PARTITION_TOKENS).  Returns 0 for
+ * invalid sizes.
+ */
+#define FA_DECODE_PARTITION_TOKENS 256
+size_t fa_paged_decode_workspace_size(int num_seqs, int num_heads, int head_size,
+                                      int max_context_len);
+
+/*
+ * fa_paged_decode -- single-query attention over a paged KV cache.
+ *
+ *   q            : [num_seqs, num_heads, head_size], element type `dtype`.
+ *   k_cache      : [num_blocks, num_kv_heads, head_size / x, block_size, x]
+ *                  with x = 16 / sizeof(element) (8 for fp16/bf16): every
+ *                  16-byte vector holds x consecutive head elements of one
+ *                  token ("PagedAttention", sections "Concepts" and "Key").
+ *   v_cache      : [num_blocks, num_kv_heads, head_size, block_size]
+ *                  ("PagedAttention", section "Value").
+ *   block_tables : [num_seqs, max_blocks_per_seq] int32: context token t of
+ *                  sequence s lives in physical block block_tables[s][t /
+ *                  block_size], slot t % block_size.
+ *   context_lens : [num_seqs] int32, each in [0, max_context_len].  Not
+ *                  checked on the device: larger values read out of range.
+ *   out          : [num_seqs, num_heads, head_size], element type `dtype`.
+ *                  out[s,h,:] = sum_t p_t V_t with p = softmax_t(scale * q[s,h]
+ *                  . K_t) over t < context_lens[s], rounded to nearest even.
+ *                  A context of length 0 gives out = 0.
+ *   num_kv_heads : divides num_heads; query head h reads kv head
+ *                  h / (num_heads / num_kv_heads).
+ *   head_size    : 128.  block_size: 16.  dtype: FA_F16 or FA_BF16.
+ *   max_blocks_per_seq * block_size >= max_context_len >= 0.
+ *   scale        : finite and >= 0.
+ *   workspace    : device buffer of at least
+ *                  fa_paged_decode_workspace_size(...) bytes, 256-byte
+ *                  aligned, that the call may overwrite; not read before it
+ *                  is written.  Concurrent calls need separate workspaces.
+ * The first ceil(context_lens[s] / block_size) entries of each table row must
+ * be valid block ids; they are not checked on the device.
+ */
+int fa_paged_decode(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, void *out,
+                    int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+                    int max_blocks_per_seq, int max_context_len, float scale, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* fa_strerror -- a static, human-readable string for a status code. */
+const char *fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,43 @@
+"""Shared helpers of the GPU parity tests: tolerances, comparisons, progress lines."""
+import sys
+
+import numpy as np
+import torch
+
+# Tolerances (absolute), per input element type, against the fp64 oracle run
+# on the same rounded inputs:
+#   fp32 inputs: max |dO| <= 1e-4 and max |dlse| <= 1e-4;
+#   bf16/fp16 inputs (fp32 accumulation): max |dO| <= 1e-2, mean |dO| <= 1e-3,
+#   max |dlse| <= 1e-3.
+TOL = {
+    torch.float32: dict(o_max=1e-4, o_mean=1e-4, lse_max=1e-4),
+    torch.bfloat16: dict(o_max=1e-2, o_mean=1e-3, lse_max=1e-3),
+    torch.float16: dict(o_max=1e-2, o_mean=1e-3, lse_max=1e-3),
+}
+DECODE_TOL = dict(o_max=1e-2, o_mean=1e-3)
+
+
+def progress(msg):
+    """A progress line that bypasses pytest's capture and is flushed at once."""
+    sys.__stderr__.write("[gpu] %s\n" % msg)
+    sys.__stderr__.flush()
+
+
+def errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    e = np.abs(got - ref)
+    return float(e.max()) if e.size else 0.0, float(e.mean()) if e.size else 0.0
+
+
+def assert_fwd_close(o, lse, o_ref, lse_ref, dtype, label=""):
+    """o, lse: GPU results (numpy fp64) at the oracle's rows; refs from the oracle."""
+    assert np.all(np.isfinite(o)), "non-finite O " + label
+    assert np.all(np.isfinite(lse)), "non-finite lse " + label
+    tol = TOL[dtype]
+    omax, omean = errors(o, o_ref)
+    lmax, _ = errors(lse, lse_ref)
+    progress("%s max|dO|=%.3g mean|dO|=%.3g max|dlse|=%.3g" % (label, omax, omean, lmax))
+    assert omax <= tol["o_max"], (label, omax)
+    assert omean <= tol["o_mean"], (label, omean)
+    assert lmax <= tol["lse_max"], (label, lmax)
+    return omax, omean, lmax

@@ -1,0 +1,185 @@
+"""GPU parity of fa_fwd against the fp64 oracle, through the C ABI.
+
+Full oracle at the small configurations and on a grid of ragged shapes
+(several tiles plus a tail); at the full headline sizes, in the launch
+configuration the benchmark times, 256 sampled query rows per head.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_12_amd as fa
+import oracle
+from exact_attention_12_amd import inputs
+from gpu_util import TOL, assert_fwd_close, progress
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    progress("start " + request.node.nodeid)
+    yield
+
+
+def run_fwd(q, k, v, scale, causal, dev):
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = fa.forward(qd, kd, vd, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def check_cfg(cfg, dev, rows=None, label=None):
+    label = label or cfg.name
+    progress("fa_fwd %s N=%d causal=%d rows=%s" % (label, cfg.N, cfg.causal,
+                                                  "all" if rows is None else len(rows)))
+    q, k, v = inputs.fwd_inputs(cfg)
+    scale = float(np.float32(cfg.scale))
+    o, lse = run_fwd(q, k, v, scale, cfg.causal, dev)
+    o_ref, l_ref = oracle.attention(q, k, v, scale, cfg.causal, rows=rows)
+    if rows is not None:
+        o, lse = o[:, :, rows], lse[:, :, rows]
+    return assert_fwd_close(o, lse, o_ref, l_ref, cfg.dtype, label)
+
+
+def test_config1_fp32(gpu, fa_lib):
+    check_cfg(inputs.FWD_CONFIGS[1], gpu)
+
+
+@pytest.mark.parametrize("N", [2048, 2000])
+def test_config2_bf16(gpu, fa_lib, N):
+    check_cfg(inputs.FWD_CONFIGS[2].replace(N=N), gpu)
+
+
+def test_config3_headline_sampled_rows(gpu, fa_lib):
+    cfg = inputs.FWD_CONFIGS[3]
+    check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
+
+
+def test_config4_long_context_sampled_rows(gpu, fa_lib):
+    cfg = inputs.FWD_CONFIGS[4]
+    check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
+
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 15, 33, 64, 65, 129, 300])
+def test_ragged_shapes(gpu, fa_lib, dt, d, causal, N):
+    cfg = inputs.FwdConfig(cid=60 + N % 17, B=2, H=3, N=N, d=d, dtype=DT[dt], causal=causal,
+                           qk_factor=1.5, name="ragged %s d%d N%d causal%d" % (dt, d, N, causal))
+    check_cfg(cfg, gpu)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_long_ragged_causal(gpu, fa_lib, dt):
+    cfg = inputs.FwdConfig(cid=70, B=1, H=4, N=1000, d=128, dtype=DT[dt], causal=True,
+                           qk_factor=2.0, name="long ragged %s" % dt)
+    check_cfg(cfg, gpu)
+
+
+# ---------------------------------------------------------------- invariants
+
+def _cfg(N=200, d=128, causal=True, dt=torch.bfloat16, cid=80):
+    return inputs.FwdConfig(cid=cid, B=1, H=2, N=N, d=d, dtype=dt, causal=causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_P2_shift_invariance(gpu, fa_lib, causal):
+    cfg = _cfg(causal=causal)
+    q, k, v = inputs.fwd_inputs(cfg)
+    k[..., -1] = 1.0
+    scale = float(np.float32(cfg.scale))
+    o1, l1 = run_fwd(q, k, v, scale, causal, gpu)
+    q2 = q.clone()
+    q2[..., -1] = (q2[..., -1].float() + 2.0).to(q.dtype)
+    # q + 2 is not always exact in bf16; the shift is taken from the stored values
+    shift = scale * (q2[..., -1].double() - q[..., -1].double()).numpy()
+    o2, l2 = run_fwd(q2, k, v, scale, causal, gpu)
+    tol = TOL[cfg.dtype]
+    assert np.abs(o1 - o2).max() <= tol["o_max"]
+    assert np.abs((l2 - l1) - shift).max() <= tol["lse_max"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_P4_constant_keys(gpu, fa_lib, causal):
+    cfg = _cfg(causal=causal)
+    q, _, v = inputs.fwd_inputs(cfg)
+    k = inputs.normal(81, (cfg.d,), 1.0, cfg.dtype).expand(cfg.B, cfg.H, cfg.N, cfg.d).contiguous()
+    scale = float(np.float32(cfg.scale))
+    o, lse = run_fwd(q, k, v, scale, causal, gpu)
+    vd = v.double().numpy()
+    n = np.arange(1, cfg.N + 1) if causal else np.full(cfg.N, cfg.N)
+    mean = (np.cumsum(vd, axis=2) / n[:, None]) if causal else vd.mean(2, keepdims=True)
+    mean = np.broadcast_to(mean, o.shape)
+    assert np.abs(o - mean).max() <= 1e-2
+    lse_ref = scale * (q.double().numpy() @ k[0, 0, 0].double().numpy()) + np.log(n)
+    assert np.abs(lse - lse_ref).max() <= 1e-3
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_P8_zero_scale(gpu, fa_lib, dt):
+    cfg = _cfg(causal=True, dt=DT[dt], d=64)
+    q, k, v = inputs.fwd_inputs(cfg)
+    o, lse = run_fwd(q, k, v, 0.0, True, gpu)
+    n = np.arange(1, cfg.N + 1)
+    mean = np.cumsum(v.double().numpy(), axis=2) / n[:, None]
+    assert np.abs(o - mean).max() <= TOL[cfg.dtype]["o_max"]
+    assert np.abs(lse - np.log(n)).max() <= TOL[cfg.dtype]["lse_max"]
+
+
+def test_P7_P12_first_row_and_single_token(gpu, fa_lib):
+    cfg = _cfg(N=300)
+    q, k, v = inputs.fwd_inputs(cfg)
+    scale = float(np.float32(cfg.scale))
+    o, lse = run_fwd(q, k, v, scale, True, gpu)
+    assert np.abs(o[:, :, 0] - v[:, :, 0].double().numpy()).max() <= 1e-6
+    s00 = scale * (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1).numpy()
+    assert np.abs(lse[:, :, 0] - s00).max() <= 1e-4
+    o1, l1 = run_fwd(q[:, :, :1].contiguous(), k[:, :, :1].contiguous(),
+                     v[:, :, :1].contiguous(), scale, False, gpu)
+    assert np.abs(o1[:, :, 0] - v[:, :, 0].double().numpy()).max() <= 1e-6
+
+
+def test_P9_key_permutation_noncausal(gpu, fa_lib):
+    cfg = _cfg(N=333, causal=False)
+    q, k, v = inputs.fwd_inputs(cfg)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(cfg.N))
+    scale = float(np.float32(cfg.scale))
+    o1, l1 = run_fwd(q, k, v, scale, False, gpu)
+    o2, l2 = run_fwd(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), scale, False, gpu)
+    assert np.abs(o1 - o2).max() <= 1e-2 and np.abs(l1 - l2).max() <= 1e-3
+
+
+def test_deterministic_and_in_bounds(gpu, fa_lib):
+    cfg = _cfg(N=777, causal=True)
+    q, k, v = (t.to(gpu) for t in inputs.fwd_inputs(cfg))
+    B, H, N, d = q.shape
+    pad = 4096
+    o_buf = torch.full((B * H * N * d + pad,), float("nan"), device=gpu)
+    l_buf = torch.full((B * H * N + pad,), float("nan"), device=gpu)
+    outs = []
+    for _ in range(3):
+        o_buf[: B * H * N * d] = 0
+        fa.fa_fwd(q, k, v, o_buf, l_buf, B, H, N, d, cfg.scale, True)
+        torch.cuda.synchronize()
+        outs.append((o_buf[: B * H * N * d].clone(), l_buf[: B * H * N].clone()))
+        assert torch.isnan(o_buf[B * H * N * d:]).all(), "write past the end of o"
+        assert torch.isnan(l_buf[B * H * N:]).all(), "write past the end of lse"
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_invalid_call_launches_nothing(gpu, fa_lib):
+    q = torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device=gpu)
+    o = torch.full((1, 1, 8, 96), 7.0, device=gpu)
+    lse = torch.full((1, 1, 8), 7.0, device=gpu)
+    with pytest.raises(fa.FAError):
+        fa.fa_fwd(q, q, q, o, lse, 1, 1, 8, 96, 0.1, False)
+    torch.cuda.synchronize()
+    assert (o == 7.0).all() and (lse == 7.0).all()
