@@ -14,6 +14,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -53,6 +55,15 @@ template <> struct Mma<__bf16> {
         for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
         return r;
     }
+    // acc + (sum of the 8 rounded values), two at a time (v_dot2 with 1, 1)
+    static __device__ __forceinline__ float sum(frag x, float acc)
+    {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[2 * i], x[2 * i + 1]}, one, acc, false);
+        return acc;
+    }
 };
 
 template <> struct Mma<_Float16> {
@@ -69,6 +80,14 @@ template <> struct Mma<_Float16> {
         for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];
         return r;
     }
+    static __device__ __forceinline__ float sum(frag x, float acc)
+    {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_amdgcn_fdot2(f16x2{x[2 * i], x[2 * i + 1]}, one, acc, false);
+        return acc;
+    }
 };
 
 template <> struct Mma<float> {
@@ -79,6 +98,7 @@ template <> struct Mma<float> {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ frag pack(const float *x) { return x[0]; }
+    static __device__ __forceinline__ float sum(frag x, float acc) { return acc + x; }
 };
 
 // Row (within a 32-row tile) held by lane-half h in accumulator register r.

@@ -10,16 +10,19 @@
 //  - one workgroup of 4 waves per (b, h, 128-row query tile); the query tile
 //    is split across the waves, 32 rows each, with no communication between
 //    waves (split-Q);
-//  - every wave keeps its Q rows in registers as matrix-core operands and
-//    streams the K/V tiles (BC keys each) that all four waves share through
-//    LDS, double buffered, with 16-byte global loads;
+//  - every wave keeps its Q rows in registers as matrix-core operands; the
+//    K/V tiles (BC keys each) that all four waves share stream from HBM
+//    straight into LDS (16-byte direct-to-LDS loads, no register staging),
+//    double buffered, row-major with an XOR swizzle of the 16-byte chunks
+//    that keeps both read patterns below free of bank conflicts;
 //  - S^T = K Q^T is formed on the matrix cores, so each lane owns one query
 //    row and 16 keys of each 32-key block: the row max and the row sum are
 //    in-lane except for one exchange between the two lane halves;
-//  - the probabilities P~ = exp(S - m_new) stay in the accumulator registers
-//    and feed O^T += V^T P~^T directly (the key order inside a tile is
-//    permuted to match the operand layout, which a sum over keys does not
-//    see); V is transposed once while it is staged into LDS;
+//  - the probabilities P~ stay in the accumulator registers and feed
+//    O^T += V^T P~^T directly.  The key order inside a tile is permuted to
+//    match the operand layout (a sum over keys does not see the order), and
+//    the V^T operand is read from the row-major V tile with the LDS
+//    transpose read (4-byte reads for fp32);
 //  - the accumulator stays unnormalised and is divided by l once at the end
 //    (FlashAttention-2, youngju.dev section 8.1);
 //  - causal: tiles entirely above the diagonal are never loaded; a wave skips
@@ -29,44 +32,53 @@
 
 namespace fa {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <typename T, int D> struct FwdCfg {
     static constexpr int KW = Mma<T>::KW;
     static constexpr int ES = (int)sizeof(T);
-    static constexpr int VEC = 16 / ES;                 // elements per 16-byte vector
-    static constexpr int NT = 256;                       // threads per workgroup
-    static constexpr int BR = 128;                       // query rows per workgroup
-    static constexpr int BC = (ES == 4) ? 32 : 64;       // keys per K/V tile
-    static constexpr int NKB = BC / 32;                  // 32-key blocks per tile
-    static constexpr int KLD = D + VEC;                  // K row stride in LDS (16 B pad)
-    static constexpr int VLD = BC + VEC;                 // V^T row stride in LDS (16 B pad)
-    static constexpr int K_ELEMS = BC * KLD;
-    static constexpr int V_ELEMS = D * VLD;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;      // one LDS buffer (elements)
-    static constexpr int QK_STEPS = D / (2 * KW);        // MFMA steps over d for S
-    static constexpr int PV_STEPS = 32 / (2 * KW);       // MFMA steps per 32-key block for PV
-    static constexpr int DB = D / 32;                    // 32-row blocks of O^T
-    static constexpr int K_CHUNKS = BC * D / VEC;        // 16-byte chunks per K tile
-    static constexpr int K_PER_T = K_CHUNKS / NT;
-    static constexpr int V_BLOCKS = (BC / 4) * (D / VEC);  // 4-key x VEC-d blocks per V tile
-    static constexpr int V_PER_T = (V_BLOCKS + NT - 1) / NT;
-    static_assert(K_CHUNKS % NT == 0, "K tile must split evenly over the workgroup");
+    static constexpr int VEC = 16 / ES;              // elements per 16-byte chunk
+    static constexpr int NT = 256;                    // threads per workgroup (4 waves)
+    static constexpr int BR = 128;                    // query rows per workgroup
+    static constexpr int BC = (ES == 4) ? 32 : 64;    // keys per K/V tile
+    static constexpr int NKB = BC / 32;               // 32-key blocks per tile
+    static constexpr int CPR = D / VEC;               // 16-byte chunks per row
+    static constexpr int ROWB = D * ES;               // bytes per K/V row in LDS
+    static constexpr int TILEB = BC * ROWB;           // bytes per K or V tile
+    static constexpr int STAGEB = 2 * TILEB;          // K + V
+    static constexpr int NLD = BC * CPR / kWave;      // direct-to-LDS loads per tile
+    static constexpr int NLD_W = NLD / 4;             // ... per wave
+    static constexpr int QK_STEPS = D / (2 * KW);     // MFMA steps over d for S
+    static constexpr int PV_STEPS = 32 / (2 * KW);    // MFMA steps per 32-key block for PV
+    static constexpr int DB = D / 32;                 // 32-row blocks of O^T
+    // waves per SIMD: two (two workgroups per CU) when the registers allow
+    static constexpr int WPE = (ES == 4 && D == 128) ? 1 : 2;
+    static_assert(NLD % 4 == 0, "tile loads must split evenly over the waves");
     static_assert(D % 32 == 0 && BC % 32 == 0, "tile shapes");
 };
 
-// Position of tile-relative key k inside a V^T row in LDS.  Key k of 32-key
-// block kb sits in accumulator register r = 4*(kk/8) + kk%4 of lane-half
-// h = (kk/4)%2 (kk = k % 32); the PV step st = r / KW consumes registers
-// [st*KW, st*KW + KW) of both halves as contraction slots h*KW + r%KW.
-template <int KW> __device__ __forceinline__ int vt_pos(int k)
+// Chunk swizzle: the 16-byte chunk c of LDS row r is stored at position
+// c ^ swz(r).  Chosen (by exhaustive search over XOR-of-shifted-row-bits
+// forms) so that the 16-byte K-operand reads (32 rows, one chunk per lane
+// half) and the 8-byte transpose reads of V (8 rows x 4 chunks) hit every
+// bank the minimum number of times.
+template <int CPR, int ES> __device__ __forceinline__ int swz(int row)
 {
-    const int kb = k / 32, kk = k % 32;
-    const int r = 4 * (kk / 8) + kk % 4;
-    const int h = (kk / 4) % 2;
-    return kb * 32 + (r / KW) * (2 * KW) + h * KW + r % KW;
+    if constexpr (ES == 2)
+        return CPR >= 16 ? ((row & 7) << 1) : (row & 7);
+    else
+        return row & 15;
 }
 
+// The reference max moves only when a tile max exceeds it by more than this
+// many powers of two (see the softmax step in the kernel).
+constexpr float kRescaleLog2 = 8.0f;
+
 template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(FwdCfg<T, D>::WPE, FwdCfg<T, D>::WPE)))
 void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                    float *__restrict__ O, float *__restrict__ LSE, int N, int num_qtiles,
                    float scale)
@@ -75,7 +87,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int KW = C::KW;
-    __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -117,98 +129,57 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     const int kend = CAUSAL ? min(N, q0 + C::BR) : N;  // keys [0, kend) can be seen
     const int ntiles = (kend + C::BC - 1) / C::BC;
 
-    // ---- staging of one K/V tile: global -> registers -> LDS -------------
-    u32x4 kr[C::K_PER_T];
-    u32x4 vr[C::V_PER_T][4];
-
-    auto load_tile = [&](int j) {
+    // ---- K/V tile j -> LDS buffer buf, straight from global memory --------
+    // Load instruction I of a tile fills LDS bytes [I*1024, I*1024 + 1024):
+    // lane l writes chunk position q = I*64 + l, i.e. row q / CPR, position
+    // q % CPR, which holds global chunk (q % CPR) ^ swz(row).  Rows past the
+    // end of the sequence re-read row N-1: their scores are masked, and the
+    // values stay finite so that 0 * V is 0.
+    auto load_tile = [&](int j, int buf) {
         const int k0 = j * C::BC;
+        char *kd = smem + buf * C::STAGEB;
+        char *vd = kd + C::TILEB;
 #pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int ci = tid + C::NT * i;
-            const int row = ci / (D / C::VEC);
-            const int cc = (ci % (D / C::VEC)) * C::VEC;
-            kr[i] = (k0 + row < N) ? *(const u32x4 *)(Kh + (int64_t)(k0 + row) * D + cc)
-                                   : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < C::V_PER_T; ++i) {
-            const int bi = tid + C::NT * i;
-            const int quad = bi / (D / C::VEC);
-            const int cc = (bi % (D / C::VEC)) * C::VEC;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + 4 * quad + r;
-                vr[i][r] = (bi < C::V_BLOCKS && key < N)
-                               ? *(const u32x4 *)(Vh + (int64_t)key * D + cc)
-                               : u32x4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < C::NLD_W; ++i) {
+            const int I = wave * C::NLD_W + i;
+            const int q = I * kWave + lane;
+            const int row = q / C::CPR;
+            const int c = (q % C::CPR) ^ swz<C::CPR, C::ES>(row);
+            const int64_t src = (int64_t)min(k0 + row, N - 1) * D + c * C::VEC;
+            __builtin_amdgcn_global_load_lds((const void *)(Kh + src), (lds_void *)(kd + I * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(Vh + src), (lds_void *)(vd + I * 1024),
+                                             16, 0, 0);
         }
     };
-
-    auto store_tile = [&](int buf) {
-        T *Ks = smem + buf * C::STAGE;
-        T *Vs = Ks + C::K_ELEMS;
-#pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int ci = tid + C::NT * i;
-            const int row = ci / (D / C::VEC);
-            const int cc = (ci % (D / C::VEC)) * C::VEC;
-            *(u32x4 *)(Ks + row * C::KLD + cc) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::V_PER_T; ++i) {
-            const int bi = tid + C::NT * i;
-            if (bi < C::V_BLOCKS) {
-                const int quad = bi / (D / C::VEC);
-                const int d0 = (bi % (D / C::VEC)) * C::VEC;
-                if constexpr (C::ES == 2) {
-                    // 4 keys x 8 d -> 8 d-rows of 4 keys; the 4 keys stay
-                    // contiguous under vt_pos<8> (it permutes whole quads).
-                    const int p0 = vt_pos<KW>(4 * quad);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int sh = 16 * (e % 2);
-                        const uint32_t a = (vr[i][0][e / 2] >> sh) & 0xffffu;
-                        const uint32_t b = (vr[i][1][e / 2] >> sh) & 0xffffu;
-                        const uint32_t c = (vr[i][2][e / 2] >> sh) & 0xffffu;
-                        const uint32_t d = (vr[i][3][e / 2] >> sh) & 0xffffu;
-                        *(u32x2 *)(Vs + (d0 + e) * C::VLD + p0) = u32x2{a | (b << 16), c | (d << 16)};
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int p = vt_pos<KW>(4 * quad + r);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            *(uint32_t *)(Vs + (d0 + e) * C::VLD + p) = vr[i][r][e];
-                    }
-                }
-            }
-        }
+    // byte offset of element e of row r in a swizzled tile
+    auto lds_off = [](int r, int e) {
+        const int cc = (e * C::ES) / 16, o = (e * C::ES) % 16;
+        return r * C::ROWB + ((cc ^ swz<C::CPR, C::ES>(r)) * 16) + o;
     };
 
     // ---- running state (per lane: one query row, partial over its keys) --
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-    float m_run = -INFINITY;   // running max of raw scores q.k
-    float mc_run = -INFINITY;  // m_run * c
-    float l_run = 0.f;         // partial row sum over this lane's keys
+    float m_ref = -INFINITY;   // reference max of the raw scores q.k (see below)
+    float mc_ref = -INFINITY;  // m_ref * c
+    float l_run = 0.f;         // partial row sum of P~ (fp32) over this lane's keys
+    float l_hat = 0.f;         // the same sum of P~ as rounded for the matrix core
     const float c = scale * kLog2e;
 
-    load_tile(0);
-    store_tile(0);
+    load_tile(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int j = 0; j < ntiles; ++j) {
-        if (j + 1 < ntiles) load_tile(j + 1);
+        if (j + 1 < ntiles) load_tile(j + 1, (j + 1) & 1);
 
         const int k0 = j * C::BC;
         const bool active = !CAUSAL || k0 <= wq_hi;
         if (active) {
-            const T *Ks = smem + (j & 1) * C::STAGE;
-            const T *Vs = Ks + C::K_ELEMS;
+            const char *Ks = smem + (j & 1) * C::STAGEB;
+            const char *Vs = Ks + C::TILEB;
 
             // S^T = K Q^T for the BC keys of the tile (raw dot products).
             f32x16 s[C::NKB];
@@ -218,7 +189,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             for (int st = 0; st < C::QK_STEPS; ++st) {
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb) {
-                    const frag a = *(const frag *)(Ks + (kb * 32 + col) * C::KLD + st * 2 * KW + h * KW);
+                    const frag a = *(const frag *)(Ks + lds_off(kb * 32 + col, st * 2 * KW + h * KW));
                     s[kb] = M::mma(a, qf[st], s[kb]);
                 }
             }
@@ -226,13 +197,16 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             // Masks: keys >= N (ragged tail) and, causal, keys > query row.
             const bool need_mask = (k0 + C::BC > N) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
             if (need_mask) {
+                // key k0 + kb*32 + acc_row(r, h) is visible iff it is <= last,
+                // last = min(query row, N - 1) (causal) or N - 1.
+                const int last = CAUSAL ? min(qrow, N - 1) : N - 1;
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
+                for (int kb = 0; kb < C::NKB; ++kb) {
+                    const int lim = last - k0 - kb * 32 - 4 * h;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb * 32 + acc_row(r, h);
-                        if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (acc_row(r, 0) > lim) s[kb][r] = -INFINITY;
+                }
             }
 
             // Row max over the tile: in-lane, then across the two halves.
@@ -243,30 +217,52 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             mx = fmaxf(mx, swap_halves(mx));
 
-            const float m_new = fmaxf(m_run, mx);
-            const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-            const float mc_new = m_safe * c;
-            const float alpha = exp2_hw(mc_run - mc_new);  // e^(scale*(m_old - m_new))
+            // Lazy reference max.  The probabilities are taken relative to a
+            // reference m_ref that only moves when some row's tile max exceeds
+            // it by more than 2^kRescaleLog2 (or on the first tile): since
+            // exp(s - m) = exp(s - m') exp(m' - m) for any m, m', the result
+            // is the same for any reference, and a stale one keeps P <= 2^8.
+            // Every row sees key 0 in tile 0, so m_ref is finite after it.
+            const bool grow = (m_ref == -INFINITY && mx != -INFINITY) ||
+                              (mx - m_ref) * c > kRescaleLog2;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float m_new = fmaxf(m_ref, mx);
+                const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+                const float mc_new = m_safe * c;
+                const float alpha = exp2_hw(mc_ref - mc_new);  // e^(scale*(m_old - m_new)); 0 at start
+                l_run *= alpha;
+                l_hat *= alpha;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+                m_ref = m_new;
+                mc_ref = mc_new;
+            }
 
-            // P~ = exp(scale*(s - m_new)) = 2^(s*c - m_new*c)
+            // P~ = exp(scale*(s - m_ref)) = 2^(s*c - m_ref*c); masked keys give 0
             float rs = 0.f;
+            if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
+                for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = exp2_hw(__builtin_fmaf(s[kb][r], c, -mc_new));
-                    if (need_mask && s[kb][r] == -INFINITY) p = 0.f;
-                    s[kb][r] = p;
-                    rs += p;
-                }
-            l_run = alpha * l_run + rs;
-            m_run = m_new;
-            mc_run = mc_new;
+                    for (int r = 0; r < 16; ++r) {
+                        const float p = exp2_hw(__builtin_fmaf(s[kb][r], c, -mc_ref));
+                        s[kb][r] = (s[kb][r] == -INFINITY) ? 0.f : p;  // also for scale 0
+                        rs += s[kb][r];
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        s[kb][r] = exp2_hw(__builtin_fmaf(s[kb][r], c, -mc_ref));
+                        rs += s[kb][r];
+                    }
+            }
+            l_run += rs;
 
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-
-            // O^T += V^T P~^T
+            // O^T += V^T P~^T.  PV step st of key block kb contracts the
+            // registers [st*KW, st*KW + KW) of both lane halves; slot
+            // h*KW + e holds key kb*32 + acc_row(st*KW + e, h).
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
@@ -275,23 +271,48 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 #pragma unroll
                     for (int e = 0; e < KW; ++e) pv[e] = s[kb][st * KW + e];
                     const frag b = M::pack(pv);
+                    l_hat = M::sum(b, l_hat);
 #pragma unroll
                     for (int db = 0; db < C::DB; ++db) {
-                        const frag a = *(const frag *)(Vs + (db * 32 + col) * C::VLD + kb * 32 +
-                                                       st * 2 * KW + h * KW);
+                        frag a;
+                        if constexpr (C::ES == 2) {
+                            // Two transpose reads, each giving this lane 4
+                            // consecutive keys of head element db*32 + col:
+                            // keys kb*32 + 16*st + 4*h (+8) + 0..3.  Source
+                            // lane r of each 16-lane group points at row
+                            // (that base + r/4), elements 4*(r%4) .. +3 of the
+                            // group's 16 head elements.
+                            const int g = lane / 16, r16 = lane % 16;
+                            const int row = kb * 32 + 16 * st + 4 * (g / 2) + r16 / 4;
+                            const int e0 = db * 32 + 16 * (g % 2) + 4 * (r16 % 4);
+                            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_s16x4 *)(Vs + lds_off(row, e0)));
+                            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_s16x4 *)(Vs + lds_off(row + 8, e0)));
+                            a = __builtin_bit_cast(
+                                frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        } else {
+                            a = *(const frag *)(Vs + lds_off(kb * 32 + acc_row(st, h), db * 32 + col));
+                        }
                         acc[db] = M::mma(a, b, acc[db]);
                     }
                 }
             }
         }
 
-        if (j + 1 < ntiles) store_tile((j + 1) & 1);
+        // this wave's loads of the next tile have landed, and after the
+        // barrier every wave's have, and nobody reads the current buffer
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
     // ---- epilogue: O = acc / l, lse = scale*m + ln l ----------------------
+    // O is normalised by the sum of the probabilities exactly as the matrix
+    // core saw them (rounded to the input type), so the output is a convex
+    // combination of the value rows with consistently rounded weights; lse
+    // uses the unrounded fp32 sum.
     const float l_tot = l_run + swap_halves(l_run);
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / (l_hat + swap_halves(l_hat));
     if (qrow < N) {
         float *orow = O + head + (int64_t)qrow * D;
 #pragma unroll
@@ -302,7 +323,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                 *(f32x4 *)(orow + d) = f32x4{acc[db][4 * r4 + 0] * inv, acc[db][4 * r4 + 1] * inv,
                                             acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv};
             }
-        if (h == 0) LSE[(int64_t)bh * N + qrow] = scale * m_run + log2_hw(l_tot) * kLn2;
+        if (h == 0) LSE[(int64_t)bh * N + qrow] = scale * m_ref + log2_hw(l_tot) * kLn2;
     }
 }
 

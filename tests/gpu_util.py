@@ -1,5 +1,5 @@
 """Shared helpers of the GPU parity tests: tolerances, comparisons, progress lines."""
-import sys
+import os
 
 import numpy as np
 import torch
@@ -17,10 +17,21 @@ TOL = {
 DECODE_TOL = dict(o_max=1e-2, o_mean=1e-3)
 
 
+_LOG = os.environ.get("FA_PROGRESS_LOG") or os.path.join(
+    os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out", "gpu_progress.log")
+
+
 def progress(msg):
-    """A progress line that bypasses pytest's capture and is flushed at once."""
-    sys.__stderr__.write("[gpu] %s\n" % msg)
-    sys.__stderr__.flush()
+    """Append a progress line (test case, shape, errors) to a log file, flushed at once.
+
+    pytest captures the test's own stdout/stderr; the file keeps the record of
+    which case ran last even if the process dies."""
+    try:
+        os.makedirs(os.path.dirname(_LOG), exist_ok=True)
+        with open(_LOG, "a") as f:
+            f.write("[gpu] %s\n" % msg)
+    except OSError:
+        pass
 
 
 def errors(got, ref):
