@@ -43,6 +43,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, "\n".join(msgs)))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+    # the library must load with every symbol resolved (a kernel whose host
+    # launch stub was not emitted shows up here, not at the first call)
+    chk = subprocess.run([sys.executable, "-c", "import ctypes, sys; ctypes.CDLL(sys.argv[1])", tmp],
+                         capture_output=True, text=True)
+    if chk.returncode != 0:
+        os.remove(tmp)
+        raise RuntimeError("built library does not load:\n" + chk.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -60,6 +60,8 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, float *o, flo
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     const int64_t qtiles = ((int64_t)N + kFwdRowsPerWorkgroup - 1) / kFwdRowsPerWorkgroup;
     if ((int64_t)B * H * qtiles > INT_MAX) return FA_ERR_UNSUPPORTED;
+    // one head of K or V is addressed with 32-bit byte offsets
+    if ((int64_t)N * d * es > INT_MAX) return FA_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(lse, 4))
         return FA_ERR_ALIGNMENT;

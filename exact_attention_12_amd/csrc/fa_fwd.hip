@@ -72,6 +72,17 @@ template <int CPR, int ES> __device__ __forceinline__ int swz(int row)
         return row & 15;
 }
 
+// Buffer resource word 3 for raw (unformatted, unswizzled) byte addressing.
+constexpr int kBufferFlags = 0x00020000;
+
+// 16 bytes per lane from buffer r at byte offset voff + soff into LDS at
+// lds + 16 * lane (the LDS base must be the same for the whole wave).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char *lds, int voff,
+                                                  int soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+
 // The reference max moves only when a tile max exceeds it by more than this
 // many powers of two (see the softmax step in the kernel).
 constexpr float kRescaleLog2 = 8.0f;
@@ -91,7 +102,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wave = tid / kWave;
+    // wave index in a scalar register: every branch on it is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int col = lane % 32;  // query row of this lane within the wave's 32
     const int h = lane / 32;    // lane half
 
@@ -132,24 +144,45 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // ---- K/V tile j -> LDS buffer buf, straight from global memory --------
     // Load instruction I of a tile fills LDS bytes [I*1024, I*1024 + 1024):
     // lane l writes chunk position q = I*64 + l, i.e. row q / CPR, position
-    // q % CPR, which holds global chunk (q % CPR) ^ swz(row).  Rows past the
-    // end of the sequence re-read row N-1: their scores are masked, and the
-    // values stay finite so that 0 * V is 0.
+    // q % CPR, which holds global chunk (q % CPR) ^ swz(row).  The element
+    // offset of that chunk relative to the tile's first row is the same for
+    // every tile.  Rows past the end of the sequence re-read row N-1: their
+    // scores are masked, and the values stay finite so that 0 * V is 0.
+    // Loads go through buffer resources (base = this head's K or V, scalar
+    // registers); the per-lane byte offset within a tile is fixed, the tile's
+    // offset is a scalar.
+    int ld_row[C::NLD_W], ld_off[C::NLD_W];
+#pragma unroll
+    for (int i = 0; i < C::NLD_W; ++i) {
+        const int q = (wave * C::NLD_W + i) * kWave + lane;
+        ld_row[i] = q / C::CPR;
+        ld_off[i] = (ld_row[i] * D + ((q % C::CPR) ^ swz<C::CPR, C::ES>(ld_row[i])) * C::VEC) * C::ES;
+    }
+    const int head_bytes = N * C::ROWB;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)Kh, 0, head_bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)Vh, 0, head_bytes, kBufferFlags);
     auto load_tile = [&](int j, int buf) {
         const int k0 = j * C::BC;
         char *kd = smem + buf * C::STAGEB;
         char *vd = kd + C::TILEB;
+        const int soff = k0 * C::ROWB;
+        if (k0 + C::BC <= N) {
 #pragma unroll
-        for (int i = 0; i < C::NLD_W; ++i) {
-            const int I = wave * C::NLD_W + i;
-            const int q = I * kWave + lane;
-            const int row = q / C::CPR;
-            const int c = (q % C::CPR) ^ swz<C::CPR, C::ES>(row);
-            const int64_t src = (int64_t)min(k0 + row, N - 1) * D + c * C::VEC;
-            __builtin_amdgcn_global_load_lds((const void *)(Kh + src), (lds_void *)(kd + I * 1024),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(Vh + src), (lds_void *)(vd + I * 1024),
-                                             16, 0, 0);
+            for (int i = 0; i < C::NLD_W; ++i) {
+                const int I = wave * C::NLD_W + i;
+                buffer_load_lds16(krs, kd + I * 1024, ld_off[i], soff);
+                buffer_load_lds16(vrs, vd + I * 1024, ld_off[i], soff);
+            }
+        } else {
+            // ragged last tile: rows >= N re-read row N-1
+#pragma unroll
+            for (int i = 0; i < C::NLD_W; ++i) {
+                const int I = wave * C::NLD_W + i;
+                const int over = k0 + ld_row[i] - (N - 1);
+                const int off = over > 0 ? ld_off[i] - over * C::ROWB : ld_off[i];
+                buffer_load_lds16(krs, kd + I * 1024, off, soff);
+                buffer_load_lds16(vrs, vd + I * 1024, off, soff);
+            }
         }
     };
     // byte offset of element e of row r in a swizzled tile
@@ -157,6 +190,19 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         const int cc = (e * C::ES) / 16, o = (e * C::ES) % 16;
         return r * C::ROWB + ((cc ^ swz<C::CPR, C::ES>(r)) * 16) + o;
     };
+    // Per-lane LDS read offsets that are the same for every tile.  The
+    // swizzle depends on the row only through row % 16, and the key-block,
+    // step and +8 row offsets below are multiples of 16 rows.
+    int k_rd[C::QK_STEPS];  // K operand of step st: row col, elements st*2KW + h*KW
+#pragma unroll
+    for (int st = 0; st < C::QK_STEPS; ++st) k_rd[st] = lds_off(col, st * 2 * KW + h * KW);
+    int v_rd[C::DB];  // 16-bit V^T transpose-read source of block db
+    {
+        const int g = lane / 16, r16 = lane % 16;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+            v_rd[db] = lds_off(4 * (g / 2) + r16 / 4, db * 32 + 16 * (g % 2) + 4 * (r16 % 4));
+    }
 
     // ---- running state (per lane: one query row, partial over its keys) --
     f32x16 acc[C::DB];
@@ -172,12 +218,14 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int j = 0; j < ntiles; ++j) {
+    // Causal: this wave's rows see no key of tiles j >= nt_w; those tiles are
+    // still loaded for the other waves (same barrier count for every wave).
+    const int nt_w = CAUSAL ? min(ntiles, wq_hi / C::BC + 1) : ntiles;
+    for (int j = 0; j < nt_w; ++j) {
         if (j + 1 < ntiles) load_tile(j + 1, (j + 1) & 1);
 
         const int k0 = j * C::BC;
-        const bool active = !CAUSAL || k0 <= wq_hi;
-        if (active) {
+        {
             const char *Ks = smem + (j & 1) * C::STAGEB;
             const char *Vs = Ks + C::TILEB;
 
@@ -189,24 +237,27 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             for (int st = 0; st < C::QK_STEPS; ++st) {
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb) {
-                    const frag a = *(const frag *)(Ks + lds_off(kb * 32 + col, st * 2 * KW + h * KW));
+                    const frag a = *(const frag *)(Ks + kb * 32 * C::ROWB + k_rd[st]);
                     s[kb] = M::mma(a, qf[st], s[kb]);
                 }
             }
 
             // Masks: keys >= N (ragged tail) and, causal, keys > query row.
+            // Key k0 + kb*32 + acc_row(r, h) is visible iff acc_row(r, 0) <=
+            // lim[kb], with last = min(query row, N - 1) (causal) or N - 1.
             const bool need_mask = (k0 + C::BC > N) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
-            if (need_mask) {
-                // key k0 + kb*32 + acc_row(r, h) is visible iff it is <= last,
-                // last = min(query row, N - 1) (causal) or N - 1.
+            int lim[C::NKB];
+            {
                 const int last = CAUSAL ? min(qrow, N - 1) : N - 1;
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
-                    const int lim = last - k0 - kb * 32 - 4 * h;
+                for (int kb = 0; kb < C::NKB; ++kb) lim[kb] = last - k0 - kb * 32 - 4 * h;
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        if (acc_row(r, 0) > lim) s[kb][r] = -INFINITY;
-                }
+                        if (acc_row(r, 0) > lim[kb]) s[kb][r] = -INFINITY;
             }
 
             // Row max over the tile: in-lane, then across the two halves.
@@ -246,7 +297,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float p = exp2_hw(__builtin_fmaf(s[kb][r], c, -mc_ref));
-                        s[kb][r] = (s[kb][r] == -INFINITY) ? 0.f : p;  // also for scale 0
+                        s[kb][r] = (acc_row(r, 0) > lim[kb]) ? 0.f : p;  // also for scale 0
                         rs += s[kb][r];
                     }
             } else {
@@ -279,16 +330,13 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                             // Two transpose reads, each giving this lane 4
                             // consecutive keys of head element db*32 + col:
                             // keys kb*32 + 16*st + 4*h (+8) + 0..3.  Source
-                            // lane r of each 16-lane group points at row
-                            // (that base + r/4), elements 4*(r%4) .. +3 of the
-                            // group's 16 head elements.
-                            const int g = lane / 16, r16 = lane % 16;
-                            const int row = kb * 32 + 16 * st + 4 * (g / 2) + r16 / 4;
-                            const int e0 = db * 32 + 16 * (g % 2) + 4 * (r16 % 4);
-                            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_s16x4 *)(Vs + lds_off(row, e0)));
-                            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_s16x4 *)(Vs + lds_off(row + 8, e0)));
+                            // lane r of each 16-lane group g points at row
+                            // kb*32 + 16*st + 4*(g/2) + r/4 (+8), elements
+                            // db*32 + 16*(g%2) + 4*(r%4) .. +3.
+                            const char *vrow = Vs + (kb * 32 + 16 * st) * C::ROWB + v_rd[db];
+                            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vrow);
+                            const s16x4 hi =
+                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vrow + 8 * C::ROWB));
                             a = __builtin_bit_cast(
                                 frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                         } else {
@@ -302,6 +350,11 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 
         // this wave's loads of the next tile have landed, and after the
         // barrier every wave's have, and nobody reads the current buffer
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    for (int j = nt_w; j < ntiles; ++j) {
+        if (j + 1 < ntiles) load_tile(j + 1, (j + 1) & 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }

@@ -69,7 +69,9 @@ enum {
  *   lse     : [B, H, N] fp32, 4-byte aligned.  Written: lse_i = m_i + ln l_i
  *             (natural log of sum_j exp(s_ij)), the per-row statistic kept
  *             for a recomputing backward pass (youngju.dev section 7.2).
- *   B, H, N : batch, heads, sequence length, each >= 1.
+ *   B, H, N : batch, heads, sequence length, each >= 1; one head of K or V
+ *             must stay below 2 GiB (N * d * sizeof(element) < 2^31) and
+ *             B * H * ceil(N / 128) below 2^31, else FA_ERR_UNSUPPORTED.
  *   d       : head dimension, 64 or 128 (else FA_ERR_UNSUPPORTED).
  *   scale   : finite and >= 0 (usually 1/sqrt(d)); else FA_ERR_INVALID_ARG.
  *   causal  : non-zero: row i sees keys j <= i only (top-left aligned square

@@ -76,6 +76,8 @@ def test_fwd_validation(fa_lib):
     assert fwd(fa_lib, o=far, lse=far + 64) == INVALID
     # grid beyond a 32-bit workgroup count
     assert fwd(fa_lib, B=1 << 16, H=1 << 16, N=1 << 10, **base) == UNSUPPORTED
+    # one head beyond 2 GiB (32-bit buffer offsets)
+    assert fwd(fa_lib, N=1 << 23, d=128, dtype=1, o=P + (1 << 40), lse=P + (1 << 41)) == UNSUPPORTED
 
 
 def dec(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=P, S=4, H=8, Hkv=8, D=128, BS=16, MB=4,
