@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (e.g. under a profiler)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 5 plain device copies of MIB MiB "
+                         "(reference kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -100,6 +103,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 5}), flush=True)
+        return
 
     import exact_attention_12_amd as fa
     from exact_attention_12_amd import inputs

@@ -60,14 +60,16 @@ template <typename T, int D> struct FwdCfg {
 };
 
 // Chunk swizzle: the 16-byte chunk c of LDS row r is stored at position
-// c ^ swz(r).  Chosen (by exhaustive search over XOR-of-shifted-row-bits
-// forms) so that the 16-byte K-operand reads (32 rows, one chunk per lane
-// half) and the 8-byte transpose reads of V (8 rows x 4 chunks) hit every
-// bank the minimum number of times.
+// c ^ swz(r).  LDS serves a 16-byte read 16 lanes per pass and an 8-byte read
+// 32 lanes per pass, 64 banks of 4 bytes each.  The form below (found by
+// exhaustive search over XOR-of-shifted-row-bit forms under that model)
+// gives both read patterns the minimum number of passes: the K operand (16
+// consecutive rows, one chunk) and the V transpose read (4 rows x 4 chunks
+// per 32 lanes).  It depends on the row only through row % 16.
 template <int CPR, int ES> __device__ __forceinline__ int swz(int row)
 {
     if constexpr (ES == 2)
-        return CPR >= 16 ? ((row & 7) << 1) : (row & 7);
+        return CPR >= 16 ? (((row & 3) << 2) ^ ((row >> 2) & 3)) : (((row & 3) << 1) ^ ((row >> 2) & 3));
     else
         return row & 15;
 }
@@ -191,17 +193,20 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         return r * C::ROWB + ((cc ^ swz<C::CPR, C::ES>(r)) * 16) + o;
     };
     // Per-lane LDS read offsets that are the same for every tile.  The
-    // swizzle depends on the row only through row % 16, and the key-block,
-    // step and +8 row offsets below are multiples of 16 rows.
+    // swizzle depends on the row only through row % 16, and the key-block and
+    // step offsets below are multiples of 16 rows.
     int k_rd[C::QK_STEPS];  // K operand of step st: row col, elements st*2KW + h*KW
 #pragma unroll
     for (int st = 0; st < C::QK_STEPS; ++st) k_rd[st] = lds_off(col, st * 2 * KW + h * KW);
-    int v_rd[C::DB];  // 16-bit V^T transpose-read source of block db
+    int v_rd[2][C::DB];  // 16-bit V^T transpose-read sources of block db (rows +0 / +8)
     {
         const int g = lane / 16, r16 = lane % 16;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-            v_rd[db] = lds_off(4 * (g / 2) + r16 / 4, db * 32 + 16 * (g % 2) + 4 * (r16 % 4));
+        for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+                v_rd[hi][db] = lds_off(8 * hi + 4 * (g / 2) + r16 / 4,
+                                       db * 32 + 16 * (g % 2) + 4 * (r16 % 4));
     }
 
     // ---- running state (per lane: one query row, partial over its keys) --
@@ -333,10 +338,11 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                             // lane r of each 16-lane group g points at row
                             // kb*32 + 16*st + 4*(g/2) + r/4 (+8), elements
                             // db*32 + 16*(g%2) + 4*(r%4) .. +3.
-                            const char *vrow = Vs + (kb * 32 + 16 * st) * C::ROWB + v_rd[db];
-                            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vrow);
+                            const char *vblk = Vs + (kb * 32 + 16 * st) * C::ROWB;
+                            const s16x4 lo =
+                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[0][db]));
                             const s16x4 hi =
-                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vrow + 8 * C::ROWB));
+                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[1][db]));
                             a = __builtin_bit_cast(
                                 frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                         } else {
