@@ -203,25 +203,42 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
 
 template <typename T> __device__ __forceinline__ T f32_to_elem(float x) { return (T)x; }
 
+// Merge of the partitions of one (sequence, head) row per 128 threads (one
+// head element each), two rows per workgroup.  Partials are read in groups of
+// 8 partitions with all loads of a group issued before they are combined.
+constexpr int kMergeRows = 2;
 template <typename T>
-__global__ __attribute__((amdgpu_flat_work_group_size(128, 128)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_decode_merge_kernel(const int32_t *__restrict__ context_lens, T *__restrict__ out,
-                            int num_heads, int nparts, DecWs ws)
+                            int rows, int num_heads, int nparts, DecWs ws)
 {
-    const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-    const int ctx = context_lens[s];
+    const int r = blockIdx.x * kMergeRows + threadIdx.x / kDecD;
+    if (r >= rows) return;
+    const int d = threadIdx.x % kDecD;
+    const int ctx = context_lens[r / num_heads];
     const int np = min(nparts, (ctx + kDecPart - 1) / kDecPart);
-    const int64_t row = (int64_t)s * num_heads + h;
-    const int64_t base = row * nparts;
+    const int64_t base = (int64_t)r * nparts;
     float m = -INFINITY;
     for (int p = 0; p < np; ++p) m = fmaxf(m, ws.m[base + p]);
     float wsum = 0.f, o = 0.f;
-    for (int p = 0; p < np; ++p) {
-        const float w = ws.l[base + p] * exp2_hw((ws.m[base + p] - m) * kLog2e);
-        wsum += w;
-        o = __builtin_fmaf(w, ws.o[(base + p) * kDecD + d], o);
+    for (int p0 = 0; p0 < np; p0 += 8) {
+        float mv[8], lv[8], ov[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int p = min(p0 + i, np - 1);
+            mv[i] = ws.m[base + p];
+            lv[i] = ws.l[base + p];
+            ov[i] = ws.o[(base + p) * kDecD + d];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (p0 + i < np) {
+                const float w = lv[i] * exp2_hw((mv[i] - m) * kLog2e);
+                wsum += w;
+                o = __builtin_fmaf(w, ov[i], o);
+            }
     }
-    out[row * kDecD + d] = f32_to_elem<T>(np > 0 ? o / wsum : 0.f);
+    out[(int64_t)r * kDecD + d] = f32_to_elem<T>(np > 0 ? o / wsum : 0.f);
 }
 
 size_t decode_workspace_bytes(int num_seqs, int num_heads, int max_context_len)
@@ -241,8 +258,8 @@ static hipError_t launch_decode(const void *q, const void *kc, const void *vc, c
     if (np == 0) {
         // every context is empty: the merge writes zeros
         DecWs ws{(float *)workspace, (float *)workspace, (float *)workspace};
-        hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3(H, S), dim3(kDecD), 0, stream, cl,
-                           (T *)out, H, 0, ws);
+        hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3((S * H + kMergeRows - 1) / kMergeRows),
+                           dim3(kMergeRows * kDecD), 0, stream, cl, (T *)out, S * H, H, 0, ws);
         return hipGetLastError();
     }
     const int64_t parts = (int64_t)S * H * np;
@@ -255,8 +272,8 @@ static hipError_t launch_decode(const void *q, const void *kc, const void *vc, c
                        ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3(H, S), dim3(kDecD), 0, stream, cl, (T *)out,
-                       H, np, ws);
+    hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3((S * H + kMergeRows - 1) / kMergeRows),
+                       dim3(kMergeRows * kDecD), 0, stream, cl, (T *)out, S * H, H, np, ws);
     return hipGetLastError();
 }
 
