@@ -69,14 +69,7 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
     const int ctx = context_lens[s];
     const int t0 = p * kDecPart;
     const int64_t pidx = ((int64_t)s * num_heads + h) * nparts + p;
-    if (t0 >= ctx) {
-        // empty partition: weight 0 in the merge
-        if (tid == 0) {
-            ws.m[pidx] = -INFINITY;
-            ws.l[pidx] = 0.f;
-        }
-        return;
-    }
+    if (t0 >= ctx) return;  // empty partition: the merge reads only partitions below ctx
     const int ntok = min(kDecPart, ctx - t0);
     const int nblk = (ntok + kDecBS - 1) / kDecBS;
     const int kvh = h / (num_heads / num_kv_heads);
