@@ -16,7 +16,7 @@ Prints ONE JSON line.  `value` is the forward pass's throughput in TFLOP/s
 (4*B*H*N^2*d / 2 for causal, per second of fa_fwd time); the decode's HBM
 bandwidth (algorithmic bytes per second of fa_paged_decode time) is reported
 under "decode".  `cpu_baseline` times the fp64 CPU oracle on a bounded sample
-of the forward workload (one head, evenly spaced query rows).
+of the forward workload (every query row of the first few heads).
 """
 import argparse
 import hashlib
@@ -60,29 +60,35 @@ def measured_traffic(kernel, src_hash):
 
 
 def cpu_baseline(q, k, v, scale, causal, target_s=12.0):
-    """Time the oracle on head (0, 0) of the forward workload, rows evenly spaced."""
+    """Time the oracle on the first heads of batch 0 of the forward workload.
+
+    A short probe (64 evenly spaced rows of one head) sizes the sample; the
+    timed sample is then every query row of the first `nh` heads, with nh
+    chosen so that it takes about target_s seconds.
+    """
     import numpy as np
     import oracle
     threads = oracle.default_threads()
-    qh, kh, vh = (t[:1, :1].contiguous() for t in (q, k, v))
-    N, d = qh.shape[2], qh.shape[3]
+    H, N, d = q.shape[1], q.shape[2], q.shape[3]
 
-    def run(R):
-        rows = np.unique(np.linspace(0, N - 1, R).round().astype(np.int64))
+    def run(nh, rows):
+        qh, kh, vh = (t[:1, :nh].contiguous() for t in (q, k, v))
         t0 = time.perf_counter()
         oracle.attention(qh, kh, vh, scale, causal, rows=rows, nthreads=threads)
         dt = time.perf_counter() - t0
-        keys = (rows + 1).sum() if causal else len(rows) * N
-        return dt, 4.0 * d * float(keys), len(rows)
+        r = np.arange(N, dtype=np.int64) if rows is None else rows
+        keys = (r + 1).sum() if causal else len(r) * N
+        return dt, 4.0 * d * float(keys) * nh
 
-    dt, fl, R = run(64)
-    R2 = int(min(N, max(64, 64 * target_s / max(dt, 1e-3))))
-    if R2 > 64:
-        dt, fl, R = run(R2)
+    probe = np.unique(np.linspace(0, N - 1, 64).round().astype(np.int64))
+    dt, fl = run(1, probe)
+    full_head = 4.0 * d * (N * (N + 1) / 2.0 if causal else float(N) * N)
+    nh = int(min(H, max(1, round(target_s / max(dt * full_head / fl, 1e-3)))))
+    dt, fl = run(nh, None)
     return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 seconds=round(dt, 3),
-                sample="fp64 oracle on head (0,0) of the forward workload: %d query rows evenly "
-                       "spaced over N=%d, causal, %.3g flop" % (R, N, fl))
+                sample="fp64 oracle on heads 0..%d of batch 0 of the forward workload "
+                       "(all %d query rows each, causal): %.3g flop" % (nh - 1, N, fl))
 
 
 def main():
