@@ -104,7 +104,27 @@ template <> struct Mma<float> {
 // Row (within a 32-row tile) held by lane-half h in accumulator register r.
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r / 4) + 4 * h + r % 4; }
 
-// Cross-half exchange: value held by lane l ^ 32.
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, kWave); }
+// The two lane halves exchange a value: both halves get op(x[l % 32],
+// x[l % 32 + 32]) with the operands in the same order, so the result is
+// bitwise the same in both.
+__device__ __forceinline__ void lane_halves(float x, float &lo, float &hi)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __builtin_bit_cast(float, (unsigned)r[0]);
+    hi = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float halves_max(float x)
+{
+    float lo, hi;
+    lane_halves(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    float lo, hi;
+    lane_halves(x, lo, hi);
+    return lo + hi;
+}
 
 }  // namespace fa

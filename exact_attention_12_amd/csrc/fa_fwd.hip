@@ -9,7 +9,9 @@
 // Work decomposition (FlashAttention-2 order, youngju.dev sections 8.2-8.3):
 //  - one workgroup of 4 waves per (b, h, 128-row query tile); the query tile
 //    is split across the waves, 32 rows each, with no communication between
-//    waves (split-Q);
+//    waves (split-Q).  Causal: a workgroup takes a heavy and a light query
+//    tile of the same head one after the other, so all workgroups carry
+//    about the same work;
 //  - every wave keeps its Q rows in registers as matrix-core operands; the
 //    K/V tiles (BC keys each) that all four waves share stream from HBM
 //    straight into LDS (16-byte direct-to-LDS loads, no register staging),
@@ -25,10 +27,19 @@
 //    transpose read (4-byte reads for fp32);
 //  - the accumulator stays unnormalised and is divided by l once at the end
 //    (FlashAttention-2, youngju.dev section 8.1);
+//  - the exponentials are taken against a reference max that is set on the
+//    first tile and moved only when a tile's probabilities would exceed
+//    2^14; the row max is not computed on the other tiles at all;
+//  - waves raise their issue priority over the matrix sections, so that the
+//    other wave on the SIMD fills the matrix pipe's shadow with its vector
+//    work rather than the reverse;
 //  - causal: tiles entirely above the diagonal are never loaded; a wave skips
 //    the arithmetic of tiles that are fully masked for its 32 rows; only
 //    diagonal and ragged-tail tiles pay for element masks.
 #include "fa_device.h"
+
+#include <type_traits>
+
 
 namespace fa {
 
@@ -85,9 +96,9 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
 }
 
-// The reference max moves only when a tile max exceeds it by more than this
-// many powers of two (see the softmax step in the kernel).
-constexpr float kRescaleLog2 = 8.0f;
+// Bound on the probabilities taken against a stale reference max (see the
+// softmax step in the kernel): 2^14, representable in every input type.
+constexpr float kPMax = 16384.0f;
 
 template <typename T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
@@ -111,37 +122,25 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 
     // Workgroup -> (b*H + h, query tile).  Consecutive workgroup ids are
     // dispatched round-robin over the 8 XCDs; remap so that the workgroups
-    // resident on one XCD (sharing its L2) work on the same head, and visit
-    // causal tiles heaviest first.
+    // resident on one XCD (sharing its L2) work on the same head.
     int wid = blockIdx.x;
     const int G = gridDim.x;
     if (G % 8 == 0) wid = (wid % 8) * (G / 8) + wid / 8;
-    const int bh = wid / num_qtiles;
-    const int ti = wid % num_qtiles;
-    const int qt = CAUSAL ? (num_qtiles - 1 - ti) : ti;
-    const int q0 = qt * C::BR;
+    // Causal: workgroup p of a head takes the query tiles nqt-1-p (heavy)
+    // and p (light) one after the other, so that every workgroup has about
+    // the same work and the grid drains evenly.
+    const int wg_per_head = CAUSAL ? (num_qtiles + 1) / 2 : num_qtiles;
+    const int bh = wid / wg_per_head;
+    const int pi = wid % wg_per_head;
 
     const int64_t head = (int64_t)bh * N * D;
     const T *Qh = Q + head;
     const T *Kh = K + head;
     const T *Vh = V + head;
 
-    const int qrow = q0 + wave * 32 + col;
-    const int wq_lo = q0 + wave * 32;  // first query row of this wave
-    const int wq_hi = wq_lo + 31;      // last query row of this wave
-
-    // Q rows of this lane as B operands: d = st*2KW + h*KW .. +KW.
+    // state of the current query tile (set per tile below)
+    int q0 = 0, qrow = 0, wq_lo = 0, wq_hi = 0, ntiles = 0;
     frag qf[C::QK_STEPS];
-#pragma unroll
-    for (int st = 0; st < C::QK_STEPS; ++st) {
-        if (qrow < N)
-            qf[st] = *(const frag *)(Qh + (int64_t)qrow * D + st * 2 * KW + h * KW);
-        else
-            qf[st] = frag{};
-    }
-
-    const int kend = CAUSAL ? min(N, q0 + C::BR) : N;  // keys [0, kend) can be seen
-    const int ntiles = (kend + C::BC - 1) / C::BC;
 
     // ---- K/V tile j -> LDS buffer buf, straight from global memory --------
     // Load instruction I of a tile fills LDS bytes [I*1024, I*1024 + 1024):
@@ -211,13 +210,192 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 
     // ---- running state (per lane: one query row, partial over its keys) --
     f32x16 acc[C::DB];
+    float m_ref, mc_ref;  // reference max of the raw scores q.k (see below), and m_ref * c
+    float l_run, l_hat;   // partial row sum of P~ (fp32), and of P~ as rounded for the matrix core
+    // c > 0 even for scale 0 (or a scale so small that c would be a
+    // denormal): -inf * c must stay -inf for masked keys.  In that range
+    // s * c rounds every probability to exactly 1 either way.
+    const float c = fmaxf(scale * kLog2e, 1e-30f);
+
+    // S^T = K Q^T for the BC keys of the tile at Ks (raw dot products).  The
+    // K operands are read from LDS in groups of two steps, one group
+    // ahead of the matrix products that use them.
+    auto qk = [&](const char *Ks, f32x16 (&s)[C::NKB]) {
+        constexpr int G = 2;
+        constexpr int NG = C::QK_STEPS / G;
+        frag kf[2][G][C::NKB];
+        auto rd = [&](int g, int b) {
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+                    kf[b][i][kb] = *(const frag *)(Ks + kb * 32 * C::ROWB + k_rd[g * G + i]);
+        };
+        rd(0, 0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) rd(g + 1, (g + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+                    s[kb] = M::mma(kf[g & 1][i][kb], qf[g * G + i], (g == 0 && i == 0) ? f32x16{} : s[kb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // Masks: keys >= N (ragged tail) and, causal, keys > query row.  Key
+    // k0 + kb*32 + acc_row(r, h) is visible iff acc_row(r, 0) <= lim[kb].
+    auto limits = [&](int k0, int (&lim)[C::NKB]) {
+        const int last = CAUSAL ? min(qrow, N - 1) : N - 1;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) lim[kb] = last - k0 - kb * 32 - 4 * h;
+    };
+    auto apply_mask = [&](f32x16 (&s)[C::NKB], const int (&lim)[C::NKB]) {
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (acc_row(r, 0) > lim[kb]) s[kb][r] = -INFINITY;
+    };
+    // Move the reference to the row max of this tile where that is larger,
+    // rescaling what was accumulated against the old reference.
+    auto rebase = [&](const f32x16 (&s)[C::NKB]) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = halves_max(mx);
+        const float m_new = fmaxf(m_ref, mx);
+        const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+        const float mc_new = m_safe * c;
+        const float alpha = exp2_hw(mc_ref - mc_new);  // e^(scale*(m_old - m_new)); 0 at start
+        l_run *= alpha;
+        l_hat *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+        m_ref = m_new;
+        mc_ref = mc_new;
+    };
+    // P~ = exp(scale*(s - m_ref)) = 2^(s*c - m_ref*c) in place; returns this
+    // lane's sum.  Masked keys (s = -inf) give 0 since c > 0.
+    auto exponentiate = [&](f32x16 (&s)[C::NKB]) {
+        float part[4];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = exp2_hw(__builtin_fmaf(s[kb][r], c, -mc_ref));
+                part[r % 4] = (kb == 0 && r < 4) ? s[kb][r] : part[r % 4] + s[kb][r];
+            }
+        return (part[0] + part[1]) + (part[2] + part[3]);
+    };
+
+    // One K/V tile: j is the tile, STAGE (= j % 2) its LDS buffer.
+    auto tile = [&](int j, auto stage_c) {
+        constexpr int STAGE = decltype(stage_c)::value;
+        if (j + 1 < ntiles) load_tile(j + 1, STAGE ^ 1);
+        const int k0 = j * C::BC;
+        const char *Ks = smem + STAGE * C::STAGEB;
+        const char *Vs = Ks + C::TILEB;
+
+        f32x16 s[C::NKB];
+        qk(Ks, s);
+        const bool need_mask = (k0 + C::BC > N) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
+        int lim[C::NKB];
+        limits(k0, lim);
+        if (need_mask) apply_mask(s, lim);
+
+        // Lazy reference max.  The probabilities are taken relative to a
+        // reference m_ref instead of the running max: exp(s - m) =
+        // exp(s - m') exp(m' - m) for any m, m', so the result does not
+        // depend on it as long as nothing overflows.  The first tile sets
+        // m_ref to its row max (every row sees key 0, so it is finite);
+        // later tiles exponentiate against the stale reference first and
+        // only if some lane's sum exceeds kPMax = 2^14 (which bounds every
+        // probability, keeping it representable even in fp16) recompute the
+        // tile's scores and move the reference.
+        if (j == 0) rebase(s);
+        float rs = exponentiate(s);
+        if (j != 0 && __builtin_amdgcn_ballot_w64(!(rs <= kPMax)) != 0) {
+            qk(Ks, s);
+            if (need_mask) apply_mask(s, lim);
+            rebase(s);
+            rs = exponentiate(s);
+        }
+        l_run += rs;
+
+        __builtin_amdgcn_s_setprio(1);
+        // O^T += V^T P~^T.  PV step st of key block kb contracts the
+        // registers [st*KW, st*KW + KW) of both lane halves; slot h*KW + e
+        // holds key kb*32 + acc_row(st*KW + e, h).
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int st = 0; st < C::PV_STEPS; ++st) {
+                float pv[KW];
+#pragma unroll
+                for (int e = 0; e < KW; ++e) pv[e] = s[kb][st * KW + e];
+                const frag b = M::pack(pv);
+                l_hat = M::sum(b, l_hat);
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) {
+                    frag a;
+                    if constexpr (C::ES == 2) {
+                        // Two transpose reads, each giving this lane 4
+                        // consecutive keys of head element db*32 + col: keys
+                        // kb*32 + 16*st + 4*h (+8) + 0..3.  Source lane r of
+                        // each 16-lane group g points at row kb*32 + 16*st +
+                        // 4*(g/2) + r/4 (+8), elements db*32 + 16*(g%2) +
+                        // 4*(r%4) .. +3.
+                        const char *vblk = Vs + (kb * 32 + 16 * st) * C::ROWB;
+                        const s16x4 lo =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[0][db]));
+                        const s16x4 hi =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[1][db]));
+                        a = __builtin_bit_cast(frag,
+                                               __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    } else {
+                        a = *(const frag *)(Vs + lds_off(kb * 32 + acc_row(st, h), db * 32 + col));
+                    }
+                    acc[db] = M::mma(a, b, acc[db]);
+                }
+            }
+        }
+
+        __builtin_amdgcn_s_setprio(0);
+        // this wave's loads of the next tile have landed, and after the
+        // barrier every wave's have, and nobody reads the current buffer
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+  for (int item = 0; item < (CAUSAL ? 2 : 1); ++item) {
+    const int qt = CAUSAL ? (item == 0 ? num_qtiles - 1 - pi : pi) : pi;
+    if (CAUSAL && item == 1 && qt == num_qtiles - 1 - pi) break;  // odd count: middle tile alone
+    q0 = qt * C::BR;
+    qrow = q0 + wave * 32 + col;
+    wq_lo = q0 + wave * 32;  // first query row of this wave
+    wq_hi = wq_lo + 31;      // last query row of this wave
+    // Q rows of this lane as B operands: d = st*2KW + h*KW .. +KW.
+#pragma unroll
+    for (int st = 0; st < C::QK_STEPS; ++st) {
+        if (qrow < N)
+            qf[st] = *(const frag *)(Qh + (int64_t)qrow * D + st * 2 * KW + h * KW);
+        else
+            qf[st] = frag{};
+    }
+    const int kend = CAUSAL ? min(N, q0 + C::BR) : N;  // keys [0, kend) can be seen
+    ntiles = (kend + C::BC - 1) / C::BC;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-    float m_ref = -INFINITY;   // reference max of the raw scores q.k (see below)
-    float mc_ref = -INFINITY;  // m_ref * c
-    float l_run = 0.f;         // partial row sum of P~ (fp32) over this lane's keys
-    float l_hat = 0.f;         // the same sum of P~ as rounded for the matrix core
-    const float c = scale * kLog2e;
+    m_ref = -INFINITY;
+    mc_ref = -INFINITY;
+    l_run = 0.f;
+    l_hat = 0.f;
 
     load_tile(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -226,140 +404,16 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // Causal: this wave's rows see no key of tiles j >= nt_w; those tiles are
     // still loaded for the other waves (same barrier count for every wave).
     const int nt_w = CAUSAL ? min(ntiles, wq_hi / C::BC + 1) : ntiles;
-    for (int j = 0; j < nt_w; ++j) {
-        if (j + 1 < ntiles) load_tile(j + 1, (j + 1) & 1);
-
-        const int k0 = j * C::BC;
-        {
-            const char *Ks = smem + (j & 1) * C::STAGEB;
-            const char *Vs = Ks + C::TILEB;
-
-            // S^T = K Q^T for the BC keys of the tile (raw dot products).
-            f32x16 s[C::NKB];
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-            for (int st = 0; st < C::QK_STEPS; ++st) {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
-                    const frag a = *(const frag *)(Ks + kb * 32 * C::ROWB + k_rd[st]);
-                    s[kb] = M::mma(a, qf[st], s[kb]);
-                }
-            }
-
-            // Masks: keys >= N (ragged tail) and, causal, keys > query row.
-            // Key k0 + kb*32 + acc_row(r, h) is visible iff acc_row(r, 0) <=
-            // lim[kb], with last = min(query row, N - 1) (causal) or N - 1.
-            const bool need_mask = (k0 + C::BC > N) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
-            int lim[C::NKB];
-            {
-                const int last = CAUSAL ? min(qrow, N - 1) : N - 1;
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) lim[kb] = last - k0 - kb * 32 - 4 * h;
-            }
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (acc_row(r, 0) > lim[kb]) s[kb][r] = -INFINITY;
-            }
-
-            // Row max over the tile: in-lane, then across the two halves.
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, swap_halves(mx));
-
-            // Lazy reference max.  The probabilities are taken relative to a
-            // reference m_ref that only moves when some row's tile max exceeds
-            // it by more than 2^kRescaleLog2 (or on the first tile): since
-            // exp(s - m) = exp(s - m') exp(m' - m) for any m, m', the result
-            // is the same for any reference, and a stale one keeps P <= 2^8.
-            // Every row sees key 0 in tile 0, so m_ref is finite after it.
-            const bool grow = (m_ref == -INFINITY && mx != -INFINITY) ||
-                              (mx - m_ref) * c > kRescaleLog2;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                const float m_new = fmaxf(m_ref, mx);
-                const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-                const float mc_new = m_safe * c;
-                const float alpha = exp2_hw(mc_ref - mc_new);  // e^(scale*(m_old - m_new)); 0 at start
-                l_run *= alpha;
-                l_hat *= alpha;
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-                m_ref = m_new;
-                mc_ref = mc_new;
-            }
-
-            // P~ = exp(scale*(s - m_ref)) = 2^(s*c - m_ref*c); masked keys give 0
-            float rs = 0.f;
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = exp2_hw(__builtin_fmaf(s[kb][r], c, -mc_ref));
-                        s[kb][r] = (acc_row(r, 0) > lim[kb]) ? 0.f : p;  // also for scale 0
-                        rs += s[kb][r];
-                    }
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        s[kb][r] = exp2_hw(__builtin_fmaf(s[kb][r], c, -mc_ref));
-                        rs += s[kb][r];
-                    }
-            }
-            l_run += rs;
-
-            // O^T += V^T P~^T.  PV step st of key block kb contracts the
-            // registers [st*KW, st*KW + KW) of both lane halves; slot
-            // h*KW + e holds key kb*32 + acc_row(st*KW + e, h).
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-                for (int st = 0; st < C::PV_STEPS; ++st) {
-                    float pv[KW];
-#pragma unroll
-                    for (int e = 0; e < KW; ++e) pv[e] = s[kb][st * KW + e];
-                    const frag b = M::pack(pv);
-                    l_hat = M::sum(b, l_hat);
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        frag a;
-                        if constexpr (C::ES == 2) {
-                            // Two transpose reads, each giving this lane 4
-                            // consecutive keys of head element db*32 + col:
-                            // keys kb*32 + 16*st + 4*h (+8) + 0..3.  Source
-                            // lane r of each 16-lane group g points at row
-                            // kb*32 + 16*st + 4*(g/2) + r/4 (+8), elements
-                            // db*32 + 16*(g%2) + 4*(r%4) .. +3.
-                            const char *vblk = Vs + (kb * 32 + 16 * st) * C::ROWB;
-                            const s16x4 lo =
-                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[0][db]));
-                            const s16x4 hi =
-                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[1][db]));
-                            a = __builtin_bit_cast(
-                                frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        } else {
-                            a = *(const frag *)(Vs + lds_off(kb * 32 + acc_row(st, h), db * 32 + col));
-                        }
-                        acc[db] = M::mma(a, b, acc[db]);
-                    }
-                }
-            }
-        }
-
-        // this wave's loads of the next tile have landed, and after the
-        // barrier every wave's have, and nobody reads the current buffer
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    int j = 0;
+    for (; j + 1 < nt_w; j += 2) {
+        tile(j, std::integral_constant<int, 0>{});
+        tile(j + 1, std::integral_constant<int, 1>{});
     }
-    for (int j = nt_w; j < ntiles; ++j) {
+    if (j < nt_w) {
+        tile(j, std::integral_constant<int, 0>{});
+        ++j;
+    }
+    for (; j < ntiles; ++j) {
         if (j + 1 < ntiles) load_tile(j + 1, (j + 1) & 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -370,8 +424,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // core saw them (rounded to the input type), so the output is a convex
     // combination of the value rows with consistently rounded weights; lse
     // uses the unrounded fp32 sum.
-    const float l_tot = l_run + swap_halves(l_run);
-    const float inv = 1.f / (l_hat + swap_halves(l_hat));
+    const float l_tot = halves_sum(l_run);
+    const float inv = 1.f / halves_sum(l_hat);
     if (qrow < N) {
         float *orow = O + head + (int64_t)qrow * D;
 #pragma unroll
@@ -384,6 +438,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             }
         if (h == 0) LSE[(int64_t)bh * N + qrow] = scale * m_ref + log2_hw(l_tot) * kLn2;
     }
+  }
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -392,7 +447,7 @@ static hipError_t launch_fwd(const void *q, const void *k, const void *v, float 
 {
     using C = FwdCfg<T, D>;
     const int nqt = (N + C::BR - 1) / C::BR;
-    const int64_t grid = (int64_t)B * H * nqt;
+    const int64_t grid = (int64_t)B * H * (CAUSAL ? (nqt + 1) / 2 : nqt);
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, o, lse, N, nqt, scale);
     return hipGetLastError();
