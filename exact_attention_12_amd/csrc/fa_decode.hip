@@ -196,42 +196,59 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
 
 template <typename T> __device__ __forceinline__ T f32_to_elem(float x) { return (T)x; }
 
-// Merge of the partitions of one (sequence, head) row per 128 threads (one
-// head element each), two rows per workgroup.  Partials are read in groups of
-// 8 partitions with all loads of a group issued before they are combined.
-constexpr int kMergeRows = 2;
+// Merge of the partitions of one (sequence, head) row per wave, four rows
+// per workgroup.  Lanes first combine the partitions' maxima and weights
+// (partition p on lane p % 64), then every lane accumulates two head
+// elements over all partitions, the weight of partition p taken from lane
+// p % 64 of the chunk.
+constexpr int kMergeRows = 4;
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_decode_merge_kernel(const int32_t *__restrict__ context_lens, T *__restrict__ out,
                             int rows, int num_heads, int nparts, DecWs ws)
 {
-    const int r = blockIdx.x * kMergeRows + threadIdx.x / kDecD;
+    const int r = blockIdx.x * kMergeRows + threadIdx.x / kWave;
     if (r >= rows) return;
-    const int d = threadIdx.x % kDecD;
+    const int lane = threadIdx.x % kWave;
     const int ctx = context_lens[r / num_heads];
     const int np = min(nparts, (ctx + kDecPart - 1) / kDecPart);
     const int64_t base = (int64_t)r * nparts;
     float m = -INFINITY;
-    for (int p = 0; p < np; ++p) m = fmaxf(m, ws.m[base + p]);
-    float wsum = 0.f, o = 0.f;
-    for (int p0 = 0; p0 < np; p0 += 8) {
-        float mv[8], lv[8], ov[8];
+    for (int p = lane; p < np; p += kWave) m = fmaxf(m, ws.m[base + p]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int p = min(p0 + i, np - 1);
-            mv[i] = ws.m[base + p];
-            lv[i] = ws.l[base + p];
-            ov[i] = ws.o[(base + p) * kDecD + d];
-        }
+    for (int off = 32; off >= 1; off /= 2) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    float wsum = 0.f;
+    float o0 = 0.f, o1 = 0.f;
+    for (int p0 = 0; p0 < np; p0 += kWave) {
+        const int p = p0 + lane;
+        const float w = (p < np) ? ws.l[base + p] * exp2_hw((ws.m[base + p] - m) * kLog2e) : 0.f;
+        wsum += w;
+        const int n = min(kWave, np - p0);
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {
+            f32x2 ov[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (p0 + i < np) {
-                const float w = lv[i] * exp2_hw((mv[i] - m) * kLog2e);
-                wsum += w;
-                o = __builtin_fmaf(w, ov[i], o);
+            for (int k = 0; k < 8; ++k) ov[k] = *(const f32x2 *)(ws.o + (base + p0 + i + k) * kDecD + 2 * lane);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float wk = __shfl(w, i + k, kWave);
+                o0 = __builtin_fmaf(wk, ov[k][0], o0);
+                o1 = __builtin_fmaf(wk, ov[k][1], o1);
             }
+        }
+        for (; i < n; ++i) {
+            const f32x2 ov = *(const f32x2 *)(ws.o + (base + p0 + i) * kDecD + 2 * lane);
+            const float wk = __shfl(w, i, kWave);
+            o0 = __builtin_fmaf(wk, ov[0], o0);
+            o1 = __builtin_fmaf(wk, ov[1], o1);
+        }
     }
-    out[(int64_t)r * kDecD + d] = f32_to_elem<T>(np > 0 ? o / wsum : 0.f);
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) wsum += __shfl_xor(wsum, off, kWave);
+    const float inv = np > 0 ? 1.f / wsum : 0.f;
+    T *orow = out + (int64_t)r * kDecD + 2 * lane;
+    orow[0] = f32_to_elem<T>(o0 * inv);
+    orow[1] = f32_to_elem<T>(o1 * inv);
 }
 
 size_t decode_workspace_bytes(int num_seqs, int num_heads, int max_context_len)
@@ -252,7 +269,7 @@ static hipError_t launch_decode(const void *q, const void *kc, const void *vc, c
         // every context is empty: the merge writes zeros
         DecWs ws{(float *)workspace, (float *)workspace, (float *)workspace};
         hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3((S * H + kMergeRows - 1) / kMergeRows),
-                           dim3(kMergeRows * kDecD), 0, stream, cl, (T *)out, S * H, H, 0, ws);
+                           dim3(kMergeRows * kWave), 0, stream, cl, (T *)out, S * H, H, 0, ws);
         return hipGetLastError();
     }
     const int64_t parts = (int64_t)S * H * np;
@@ -266,7 +283,7 @@ static hipError_t launch_decode(const void *q, const void *kc, const void *vc, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3((S * H + kMergeRows - 1) / kMergeRows),
-                       dim3(kMergeRows * kDecD), 0, stream, cl, (T *)out, S * H, H, np, ws);
+                       dim3(kMergeRows * kWave), 0, stream, cl, (T *)out, S * H, H, np, ws);
     return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -55,6 +56,17 @@ template <> struct Mma<__bf16> {
         for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
         return r;
     }
+    // two fp32 -> two bf16 in one 32-bit word (round to nearest even)
+    static __device__ __forceinline__ uint32_t pack2(float a, float b)
+    {
+        return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+    }
+    // acc + the two values of a packed word
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc)
+    {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+    }
     // acc + (sum of the 8 rounded values), two at a time (v_dot2 with 1, 1)
     static __device__ __forceinline__ float sum(frag x, float acc)
     {
@@ -79,6 +91,15 @@ template <> struct Mma<_Float16> {
 #pragma unroll
         for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];
         return r;
+    }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b)
+    {
+        return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
+    }
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc)
+    {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
     }
     static __device__ __forceinline__ float sum(frag x, float acc)
     {
