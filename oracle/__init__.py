@@ -26,8 +26,11 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(_HERE, "oracle.c")
-LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_TEST_SOURCE names a modified copy of oracle.c to build and load
+# instead (the mutation tests plant a mistake there and expect a pin to fail).
+_SRC_OVERRIDE = os.environ.get("ORACLE_TEST_SOURCE")
+SRC = _SRC_OVERRIDE or os.path.join(_HERE, "oracle.c")
+LIB = (os.path.splitext(_SRC_OVERRIDE)[0] + ".so") if _SRC_OVERRIDE else os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 OR_F32, OR_BF16, OR_F16, OR_F64 = 0, 1, 2, 3

@@ -1,0 +1,90 @@
+"""The oracle's pins catch planted mistakes.
+
+Each case copies oracle/oracle.c to a temporary directory, plants one
+plausible mistake (an off-by-one in the causal mask, a dropped scale, log
+base 2, a transposed or wrong operand, a wrong index in the paged layout, a
+wrong sign in an online rescale, ...), builds that copy and runs the pin
+suites (tests/test_oracle_pins.py, test_oracle_decode.py,
+test_oracle_tiling.py) against it in a subprocess.  The mutation passes only
+if at least one pin fails.  A control run of the unmodified copy must pass.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+PIN_SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_decode.py",
+              "tests/test_oracle_tiling.py"]
+
+# (name, text in oracle.c, replacement); the text must occur in the source
+MUTATIONS = [
+    ("causal_mask_excludes_diagonal",
+     "int64_t n = x->causal ? (i + 1 < x->N ? i + 1 : x->N) : x->N;",
+     "int64_t n = x->causal ? (i < x->N ? i : x->N) : x->N;"),
+    ("scale_dropped",
+     "s[j] = x->scale * dot;",
+     "s[j] = dot;"),
+    ("scores_use_q_twice",
+     "or_load(x->k, x->dtype, base + j * x->d + c)",
+     "or_load(x->q, x->dtype, base + j * x->d + c)"),
+    ("max_not_subtracted_in_lse",
+     "    return m + log(l);\n}",
+     "    return log(l);\n}"),
+    ("lse_log2",
+     "    return m + log(l);\n}",
+     "    return m + log2(l);\n}"),
+    ("output_not_normalised",
+     "o[c] = acc / l;",
+     "o[c] = acc;"),
+    ("value_columns_reversed",
+     "return or_load(dv->v, dv->dtype, dv->base + j * dv->d + c);",
+     "return or_load(dv->v, dv->dtype, dv->base + j * dv->d + (dv->d - 1 - c));"),
+    ("fp16_exponent_bias",
+     "mag = ldexp((double)(1024 + f), e - 25);",
+     "mag = ldexp((double)(1024 + f), e - 24);"),
+    ("tiled_fa1_rescale_sign",
+     "double a_old = exp(m[i] - mnew);",
+     "double a_old = exp(mnew - m[i]);"),
+    ("tiled_fa2_rescale_sign",
+     "double alpha = exp(m - mnew);",
+     "double alpha = exp(mnew - m);"),
+    ("decode_kv_head_mapping",
+     "int kvh = h / (x->H / x->Hkv);",
+     "int kvh = h % x->Hkv;"),
+    ("decode_k_layout_chunk_swapped",
+     "+ e / x->x) * x->BS + off) * x->x) + e % x->x;",
+     "+ e % x->x) * x->BS + off) * x->x) + e / x->x;"),
+    ("decode_v_token_off_by_one",
+     "or_v_index(x, blk, pv->kvh, e, (int)(t % x->BS))",
+     "or_v_index(x, blk, pv->kvh, e, (int)((t + 1) % x->BS))"),
+    ("merge_ignores_partition_sums",
+     "double w = x->part_l[item * x->P + p] * exp(x->part_m[item * x->P + p] - m_all);",
+     "double w = exp(x->part_m[item * x->P + p] - m_all);"),
+]
+
+
+def run_pins(tmp_path, source_text):
+    d = tmp_path / "oracle_copy"
+    d.mkdir(exist_ok=True)
+    src = d / "oracle.c"
+    src.write_text(source_text)
+    env = dict(os.environ, ORACLE_TEST_SOURCE=str(src), PYTHONDONTWRITEBYTECODE="1")
+    cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu"] + PIN_SUITES
+    return subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_control_copy_passes(tmp_path):
+    res = run_pins(tmp_path, open(SRC).read())
+    assert res.returncode == 0, res.stdout[-3000:] + res.stderr[-3000:]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) >= 1, "mutation site not found: " + name
+    mutated = text.replace(old, new, 1)
+    res = run_pins(tmp_path, mutated)
+    assert res.returncode != 0, "no pin failed for mutation %s:\n%s" % (name, res.stdout[-2000:])
