@@ -6,7 +6,9 @@ One step = one pass of the whole path over one batch of synthetic input:
      causal, scale 1/sqrt(128), Q/K/V iid N(0,1);
   2. fa_paged_decode on the decode workload: 64 sequences x 32 heads, head
      size 128, fp16, block size 16, context lengths uniform in [512, 4096],
-     a 20000-block pool addressed through a random permutation.
+     a 20000-block pool addressed through a random permutation;
+  3. fa_paged_decode on the grouped-query variant: the same shape with 8 kv
+     heads (4 query heads per kv head).
 Inputs are generated on the host with fixed seeds and copied to HBM before
 the timed region.  The timed region runs K steps between two device
 synchronisations; each kernel call is bracketed by HIP events recorded on the
@@ -155,6 +157,18 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     del dec["k_cache"], dec["v_cache"]
 
+    gcfg = inputs.DECODE_GQA_CONFIG
+    log("generating grouped-query decode inputs: " + gcfg.name)
+    gdec = inputs.decode_inputs(gcfg)
+    gq, gk, gv = gdec["q"].to(dev), gdec["k_cache"].to(dev), gdec["v_cache"].to(dev)
+    gbt, gcl = gdec["block_tables"].to(dev), gdec["context_lens"].to(dev)
+    gmaxctx = gdec["max_context_len"]
+    gHkv, gMB = gk.shape[1], gbt.shape[1]
+    gout = torch.empty_like(gq)
+    gws = torch.empty(fa.fa_paged_decode_workspace_size(S, Hq, D, gmaxctx), dtype=torch.uint8,
+                      device=dev)
+    del gdec["k_cache"], gdec["v_cache"]
+
     stream = torch.cuda.current_stream()
 
     def step(evs=None):
@@ -167,13 +181,17 @@ def main():
                            stream=stream)
         if evs:
             evs[2].record(stream)
+        fa.fa_paged_decode(gq, gk, gv, gbt, gcl, gout, S, Hq, gHkv, D, BS, gMB, gmaxctx, dscale, gws,
+                           stream=stream)
+        if evs:
+            evs[3].record(stream)
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -183,11 +201,14 @@ def main():
     wall = time.perf_counter() - t0
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    gqa_ms = [e[2].elapsed_time(e[3]) for e in evs]
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
+    gqa_avg = sum(gqa_ms) / len(gqa_ms)
 
     # quick sanity of the last step's results (full parity lives in the tests)
-    finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item())
+    finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item()
+                  and torch.isfinite(gout).all().item())
 
     flops = fcfg.flops()
     tflops = flops / (fwd_avg * 1e-3) / 1e12
@@ -197,6 +218,11 @@ def main():
                  + S * Hq * D * esz * 2                      # q read, out written
                  + int(((ctx + BS - 1) // BS).sum()) * 4 + S * 4)  # table entries, lengths
     dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+    gctx = gdec["context_lens"].numpy().astype(np.int64)
+    gqa_bytes = (int(gctx.sum()) * gHkv * D * esz * 2            # K and V once per kv head
+                 + S * Hq * D * esz * 2
+                 + int(((gctx + BS - 1) // BS).sum()) * 4 + S * 4)
+    gqa_gbs = gqa_bytes / (gqa_avg * 1e-3) / 1e9
 
     fwd_hash = source_hash("fa_fwd.hip", "fa_device.h")
     dec_hash = source_hash("fa_decode.hip", "fa_device.h")
@@ -241,6 +267,15 @@ def main():
                                 "traffic": dec_traffic,
                                 "kernel": "fa_decode_partition_kernel + fa_decode_merge_kernel",
                                 "algorithmic_per_launch": dec_bytes}},
+        "decode_gqa": {"metric": "paged decode HBM bandwidth, 4 query heads per kv head",
+                       "value": round(gqa_gbs, 1), "unit": "GB/s",
+                       "workload": gcfg.name, "sum_ctx": int(gctx.sum()),
+                       "ms_avg": round(gqa_avg, 4), "ms_min": round(min(gqa_ms), 4),
+                       "roofline": {"bound": "hbm", "achieved": round(gqa_gbs, 1),
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(gqa_gbs / PEAK_HBM_GBS, 4),
+                                    "kernel": "fa_decode_gqa_partition_kernel + fa_decode_merge_kernel",
+                                    "algorithmic_per_launch": gqa_bytes}},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -194,6 +194,190 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
     }
 }
 
+// Grouped-query variant (num_heads / num_kv_heads = G > 1): one workgroup per
+// (kv head, sequence, partition) serves up to GM query heads of the group,
+// so each K/V block is read from HBM once per kv head instead of once per
+// query head.  The lane maps and the per-head softmax are those of the
+// kernel above; the queries sit in LDS (fp32) instead of registers, and every
+// head has its own logits row, reductions and partial.
+template <typename T, int GM>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict__ kc,
+                                    const T *__restrict__ vc, const int32_t *__restrict__ block_tables,
+                                    const int32_t *__restrict__ context_lens, int num_heads,
+                                    int num_kv_heads, int max_blocks_per_seq, int nparts,
+                                    float scale, DecWs ws)
+{
+    const int G = num_heads / num_kv_heads;
+    const int ngroups = (G + GM - 1) / GM;
+    const int kvh = blockIdx.x / ngroups, g0 = (blockIdx.x % ngroups) * GM;
+    const int ng = min(GM, G - g0);  // query heads of this workgroup: kvh*G + g0 + g, g < ng
+    const int s = blockIdx.y, p = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int ctx = context_lens[s];
+    const int t0 = p * kDecPart;
+    if (t0 >= ctx) return;  // empty partition: the merge reads only partitions below ctx
+    const int ntok = min(kDecPart, ctx - t0);
+    const int nblk = (ntok + kDecBS - 1) / kDecBS;
+    const int h0 = kvh * G + g0;
+
+    __shared__ int tbl[kDecBlk];
+    __shared__ __attribute__((aligned(16))) float qs[GM][kDecD];
+    __shared__ __attribute__((aligned(16))) float logits[GM][kDecPart];
+    __shared__ float red[2][GM][kDecWaves];
+    __shared__ float part[kDecWaves][GM][kDecD];
+
+    if (tid < nblk) tbl[tid] = block_tables[(int64_t)s * max_blocks_per_seq + t0 / kDecBS + tid];
+    for (int i = tid; i < ng * kDecD; i += kDecThreads) {
+        const int g = i / kDecD, e = i % kDecD;
+        const T *qp = q + ((int64_t)s * num_heads + h0 + g) * kDecD;
+        qs[g][e] = (float)qp[e];
+    }
+    __syncthreads();
+
+    u32x4 kr[kDecBPW][4], vr[kDecBPW][4];
+#pragma unroll
+    for (int i = 0; i < kDecBPW; ++i) {
+        const int b = wave + kDecWaves * i;
+        if (b < nblk) {
+            const int64_t base = ((int64_t)tbl[b] * num_kv_heads + kvh) * (kDecD * kDecBS);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                kr[i][c] = *(const u32x4 *)(kc + base + (lane + 64 * c) * 8);
+                vr[i][c] = *(const u32x4 *)(vc + base + (lane + 64 * c) * 8);
+            }
+        }
+    }
+
+    // logits per head: lane l dots token l % 16 with head groups l/16 + 4c
+    float wmax[GM];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) wmax[g] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kDecBPW; ++i) {
+        const int b = wave + kDecWaves * i;
+        if (b < nblk) {
+            float kf[4][8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kf[c][e] = vec_elem<T>(kr[i][c], e);
+            const int tok = t0 + b * kDecBS + lane % 16;
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                if (g < ng) {
+                    float dot = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const f32x4 qa = *(const f32x4 *)(&qs[g][(lane / 16 + 4 * c) * 8]);
+                        const f32x4 qb = *(const f32x4 *)(&qs[g][(lane / 16 + 4 * c) * 8 + 4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            dot = __builtin_fmaf(qa[e], kf[c][e], dot);
+                            dot = __builtin_fmaf(qb[e], kf[c][e + 4], dot);
+                        }
+                    }
+                    dot += __shfl_xor(dot, 16, kWave);
+                    dot += __shfl_xor(dot, 32, kWave);
+                    const float lg = (tok < ctx) ? scale * dot : -INFINITY;
+                    if (lane < 16) logits[g][b * kDecBS + lane] = lg;
+                    wmax[g] = fmaxf(wmax[g], lg);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+#pragma unroll
+        for (int off = 8; off >= 1; off /= 2) wmax[g] = fmaxf(wmax[g], __shfl_xor(wmax[g], off, kWave));
+        if (lane == 0) red[0][g][wave] = wmax[g];
+    }
+    __syncthreads();
+
+    // p_t = exp(logit_t - m_g), l_g = sum_t p_t, one token per thread, per head
+    float l_p[GM];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        float m_g = red[0][g][0];
+#pragma unroll
+        for (int w = 1; w < kDecWaves; ++w) m_g = fmaxf(m_g, red[0][g][w]);
+        float pt = 0.f;
+        if (g < ng && tid < nblk * kDecBS) {
+            pt = exp2_hw((logits[g][tid] - m_g) * kLog2e);
+            logits[g][tid] = pt;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off /= 2) pt += __shfl_xor(pt, off, kWave);
+        if (lane == 0) red[1][g][wave] = pt;
+        wmax[g] = m_g;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        l_p[g] = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) l_p[g] += red[1][g][w];
+    }
+
+    // acc[g][c] = sum_t p_t V_t[e], e = lane/2 + 32c, tokens 8*(lane%2) .. +7 of each block
+    float acc[GM][4];
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[g][c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kDecBPW; ++i) {
+        const int b = wave + kDecWaves * i;
+        if (b < nblk) {
+            const int tb = b * kDecBS + 8 * (lane % 2);
+            const int nvalid = ntok - tb;
+            // tokens >= ntok are outside the context (their cache slots may
+            // hold anything): their values are replaced by 0, and p_t = 0
+            float vf[4][8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[c][e] = (e < nvalid) ? vec_elem<T>(vr[i][c], e) : 0.f;
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                if (g < ng) {
+                    const f32x4 pa = *(const f32x4 *)(&logits[g][tb]);
+                    const f32x4 pb = *(const f32x4 *)(&logits[g][tb + 4]);
+                    const float pw[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[g][c] = __builtin_fmaf(pw[e], vf[c][e], acc[g][c]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            acc[g][c] += __shfl_xor(acc[g][c], 1, kWave);
+            if (lane % 2 == 0) part[wave][g][lane / 2 + 32 * c] = acc[g][c];
+        }
+    __syncthreads();
+    if (tid < kDecD) {
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            if (g < ng) {
+                float o = 0.f;
+#pragma unroll
+                for (int w = 0; w < kDecWaves; ++w) o += part[w][g][tid];
+                const int64_t pidx = ((int64_t)s * num_heads + h0 + g) * nparts + p;
+                ws.o[pidx * kDecD + tid] = o / l_p[g];
+                if (tid == 0) {
+                    ws.m[pidx] = wmax[g];
+                    ws.l[pidx] = l_p[g];
+                }
+            }
+        }
+    }
+}
+
 template <typename T> __device__ __forceinline__ T f32_to_elem(float x) { return (T)x; }
 
 // Merge of the partitions of one (sequence, head) row per wave, four rows
@@ -277,9 +461,26 @@ static hipError_t launch_decode(const void *q, const void *kc, const void *vc, c
     char *w = (char *)workspace;
     DecWs ws{(float *)w, (float *)(w + up(parts * kDecD * 4)),
              (float *)(w + up(parts * kDecD * 4) + up(parts * 4))};
-    hipLaunchKernelGGL(fa_decode_partition_kernel<T>, dim3(H, S, np), dim3(kDecThreads), 0, stream,
-                       (const T *)q, (const T *)kc, (const T *)vc, bt, cl, H, Hkv, MB, np, scale,
-                       ws);
+    const int G = H / Hkv;
+    if (G == 1) {
+        hipLaunchKernelGGL(fa_decode_partition_kernel<T>, dim3(H, S, np), dim3(kDecThreads), 0,
+                           stream, (const T *)q, (const T *)kc, (const T *)vc, bt, cl, H, Hkv, MB,
+                           np, scale, ws);
+    } else {
+        // one workgroup per (kv head, group of up to GM query heads)
+        auto gqa = [&](auto kern, int gm) {
+            const int ngroups = (G + gm - 1) / gm;
+            hipLaunchKernelGGL(kern, dim3(Hkv * ngroups, S, np), dim3(kDecThreads), 0, stream,
+                               (const T *)q, (const T *)kc, (const T *)vc, bt, cl, H, Hkv, MB, np,
+                               scale, ws);
+        };
+        if (G <= 2)
+            gqa(fa_decode_gqa_partition_kernel<T, 2>, 2);
+        else if (G <= 4)
+            gqa(fa_decode_gqa_partition_kernel<T, 4>, 4);
+        else
+            gqa(fa_decode_gqa_partition_kernel<T, 8>, 8);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fa_decode_merge_kernel<T>, dim3((S * H + kMergeRows - 1) / kMergeRows),

@@ -117,6 +117,10 @@ class DecodeConfig:
 
 
 DECODE_CONFIG = DecodeConfig()
+# grouped-query variant: 4 query heads per kv head
+DECODE_GQA_CONFIG = DecodeConfig(cid=6, num_kv_heads=8,
+                                 name="64 seqs, 32 query heads / 8 kv heads, head 128, fp16, block 16, "
+                                      "ctx U[512,4096], 20000-block pool")
 
 
 def decode_inputs(cfg: DecodeConfig = DECODE_CONFIG, context_lens=None):

@@ -59,6 +59,17 @@ def test_edge_context_lengths(gpu, fa_lib, dt, Hkv):
     assert torch.all(out[0] == 0)  # empty context
 
 
+@pytest.mark.parametrize("H,Hkv", [(12, 4), (8, 1), (32, 2), (16, 8)],
+                         ids=["G3", "MQA-G8", "G16", "G2"])
+def test_grouped_query_heads(gpu, fa_lib, H, Hkv):
+    # query heads sharing a kv head are served by one workgroup (groups of up
+    # to 8; G = 16 needs two workgroups per kv head)
+    cfg = inputs.DecodeConfig(cid=95, num_seqs=6, num_heads=H, num_kv_heads=Hkv, num_blocks=1600,
+                              ctx_lo=1, ctx_hi=3000)
+    d = inputs.decode_inputs(cfg, context_lens=[1, 17, 256, 700, 2049, 3000])
+    check(d, cfg, gpu, "gqa H%d Hkv%d" % (H, Hkv))
+
+
 def test_all_contexts_empty(gpu, fa_lib):
     cfg = inputs.DecodeConfig(cid=91, num_seqs=3, num_heads=4, num_kv_heads=4, num_blocks=8,
                               ctx_lo=0, ctx_hi=16)
