@@ -8,7 +8,8 @@ One step = one pass of the whole path over one batch of synthetic input:
      size 128, fp16, block size 16, context lengths uniform in [512, 4096],
      a 20000-block pool addressed through a random permutation;
   3. fa_paged_decode on the grouped-query variant: the same shape with 8 kv
-     heads (4 query heads per kv head).
+     heads (4 query heads per kv head);
+  4. fa_fwd_gqa on the forward workload with 8 kv heads (fwd_gqa).
 Inputs are generated on the host with fixed seeds and copied to HBM before
 the timed region.  The timed region runs K steps between two device
 synchronisations; each kernel call is bracketed by HIP events recorded on the
@@ -157,6 +158,13 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     del dec["k_cache"], dec["v_cache"]
 
+    qcfg = inputs.FWD_GQA_CONFIG
+    log("generating grouped-query forward inputs: " + qcfg.name)
+    gfq, gfk, gfv = (t.to(dev) for t in inputs.fwd_inputs(qcfg))
+    gHkv_f = gfk.shape[1]
+    go = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    glse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
     gcfg = inputs.DECODE_GQA_CONFIG
     log("generating grouped-query decode inputs: " + gcfg.name)
     gdec = inputs.decode_inputs(gcfg)
@@ -185,13 +193,16 @@ def main():
                            stream=stream)
         if evs:
             evs[3].record(stream)
+        fa.fa_fwd_gqa(gfq, gfk, gfv, go, glse, B, H, gHkv_f, N, d, fscale, True, stream=stream)
+        if evs:
+            evs[4].record(stream)
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -205,10 +216,12 @@ def main():
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
     gqa_avg = sum(gqa_ms) / len(gqa_ms)
+    fgqa_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    fgqa_avg = sum(fgqa_ms) / len(fgqa_ms)
 
     # quick sanity of the last step's results (full parity lives in the tests)
     finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item()
-                  and torch.isfinite(gout).all().item())
+                  and torch.isfinite(gout).all().item() and torch.isfinite(go).all().item())
 
     flops = fcfg.flops()
     tflops = flops / (fwd_avg * 1e-3) / 1e12
@@ -267,6 +280,16 @@ def main():
                                 "traffic": dec_traffic,
                                 "kernel": "fa_decode_partition_kernel + fa_decode_merge_kernel",
                                 "algorithmic_per_launch": dec_bytes}},
+        "fwd_gqa": {"metric": "attention forward TFLOP/s, 4 query heads per kv head",
+                    "value": round(qcfg.flops() / (fgqa_avg * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                    "workload": qcfg.name, "kernel_ms_avg": round(fgqa_avg, 4),
+                    "kernel_ms_min": round(min(fgqa_ms), 4),
+                    "roofline": {"bound": "mfma",
+                                 "achieved": round(qcfg.flops() / (fgqa_avg * 1e-3) / 1e12, 2),
+                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(qcfg.flops() / (fgqa_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                 "kernel": "fa_fwd_kernel<bf16,128,causal> (grouped kv heads)",
+                                 "algorithmic_per_launch": qcfg.flops()}},
         "decode_gqa": {"metric": "paged decode HBM bandwidth, 4 query heads per kv head",
                        "value": round(gqa_gbs, 1), "unit": "GB/s",
                        "workload": gcfg.name, "sum_ctx": int(gctx.sum()),

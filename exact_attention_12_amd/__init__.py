@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = [
-    "FA_F32", "FA_BF16", "FA_F16", "FA_DECODE_PARTITION_TOKENS", "FAError",
+    "FA_F32", "FA_BF16", "FA_F16", "FA_DECODE_PARTITION_TOKENS", "FAError", "fa_fwd_gqa",
     "fa_fwd", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror",
     "forward", "paged_decode", "lib_path", "load_library",
 ]
@@ -57,6 +57,8 @@ def load_library():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_gqa.restype = i
     lib.fa_paged_decode_workspace_size.argtypes = [i, i, i, i]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
@@ -112,6 +114,17 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype=None, stream=None):
         raise FAError(st, "fa_fwd")
 
 
+def fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype=None, stream=None):
+    """C entry point ``fa_fwd_gqa``: fa_fwd with k, v of Hkv heads ([B, Hkv, N, d])."""
+    if dtype is None:
+        dtype = _dtype_code(q.dtype)
+    st = load_library().fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                   int(Hkv), int(N), int(d), float(scale), int(bool(causal)),
+                                   int(dtype), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_fwd_gqa")
+
+
 def fa_paged_decode_workspace_size(num_seqs, num_heads, head_size, max_context_len) -> int:
     """C entry point ``fa_paged_decode_workspace_size`` (bytes; 0 if invalid)."""
     return int(load_library().fa_paged_decode_workspace_size(
@@ -145,12 +158,16 @@ def _check_dev(name, t, dtype=None):
 
 
 def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
-    """Allocate o (fp32) and lse (fp32) and run ``fa_fwd``; returns (o, lse)."""
+    """Allocate o (fp32) and lse (fp32) and run ``fa_fwd`` (``fa_fwd_gqa`` when
+    k and v have fewer heads than q); returns (o, lse)."""
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(n, t, q.dtype)
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, N, d] and k, v one [B, Hkv, N, d] shape")
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d) or H % Hkv != 0:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -159,7 +176,10 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_dev("out", out, torch.float32)
     _check_dev("lse", lse, torch.float32)
-    fa_fwd(q, k, v, out, lse, B, H, N, d, scale, causal, stream=stream)
+    if Hkv == H:
+        fa_fwd(q, k, v, out, lse, B, H, N, d, scale, causal, stream=stream)
+    else:
+        fa_fwd_gqa(q, k, v, out, lse, B, H, Hkv, N, d, scale, causal, stream=stream)
     return out, lse
 
 

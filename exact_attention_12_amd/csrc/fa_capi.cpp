@@ -12,7 +12,7 @@
 
 namespace fa {
 hipError_t fwd_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
-                        int H, int N, int d, float scale, int causal, int dtype,
+                        int H, int Hkv, int N, int d, float scale, int causal, int dtype,
                         hipStream_t stream);
 hipError_t decode_dispatch(const void *q, const void *kc, const void *vc, const int32_t *bt,
                            const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
@@ -49,11 +49,15 @@ bool valid_scale(float s) { return std::isfinite(s) && s >= 0.f; }
 
 }  // namespace
 
-extern "C" int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B,
-                      int H, int N, int d, float scale, int causal, int dtype, void *stream)
+namespace {
+
+// Validation shared by fa_fwd (Hkv = H) and fa_fwd_gqa, then the launch.
+int fwd_checked(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
+                int Hkv, int N, int d, float scale, int causal, int dtype, void *stream)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-    if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
     if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
     const int es = elem_bytes(dtype);
     if (es == 0) return FA_ERR_INVALID_ARG;
@@ -65,15 +69,33 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, float *o, flo
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(lse, 4))
         return FA_ERR_ALIGNMENT;
-    const uint64_t rows = (uint64_t)B * H * N;
-    const uint64_t in_bytes = rows * d * es, o_bytes = rows * d * 4, l_bytes = rows * 4;
+    const uint64_t rows = (uint64_t)B * H * N, kv_rows = (uint64_t)B * Hkv * N;
+    const uint64_t q_bytes = rows * d * es, kv_bytes = kv_rows * d * es;
+    const uint64_t o_bytes = rows * d * 4, l_bytes = rows * 4;
     if (overlap(o, o_bytes, lse, l_bytes)) return FA_ERR_INVALID_ARG;
-    for (const void *in : {q, k, v})
-        if (overlap(o, o_bytes, in, in_bytes) || overlap(lse, l_bytes, in, in_bytes))
+    const void *ins[3] = {q, k, v};
+    const uint64_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(o, o_bytes, ins[i], in_bytes[i]) || overlap(lse, l_bytes, ins[i], in_bytes[i]))
             return FA_ERR_INVALID_ARG;
-    const hipError_t e = fa::fwd_dispatch(q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0,
-                                          dtype, (hipStream_t)stream);
+    const hipError_t e = fa::fwd_dispatch(q, k, v, o, lse, B, H, Hkv, N, d, scale,
+                                          causal ? 1 : 0, dtype, (hipStream_t)stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B,
+                      int H, int N, int d, float scale, int causal, int dtype, void *stream)
+{
+    return fwd_checked(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
+}
+
+extern "C" int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse,
+                          int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+                          void *stream)
+{
+    return fwd_checked(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype, stream);
 }
 
 extern "C" size_t fa_paged_decode_workspace_size(int num_seqs, int num_heads, int head_size,

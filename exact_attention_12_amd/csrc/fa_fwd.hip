@@ -105,7 +105,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(FwdCfg<T, D>::WPE, FwdCfg<T, D>::WPE)))
 void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                    float *__restrict__ O, float *__restrict__ LSE, int N, int num_qtiles,
-                   float scale)
+                   float scale, int H, int group)
 {
     using C = FwdCfg<T, D>;
     using M = Mma<T>;
@@ -133,10 +133,13 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     const int bh = wid / wg_per_head;
     const int pi = wid % wg_per_head;
 
+    // Q, O, lse: head bh = b*H + h.  K, V: kv head b*(H/group) + h/group
+    // (group query heads share one kv head; group = 1 is multi-head attention).
     const int64_t head = (int64_t)bh * N * D;
+    const int64_t kv_head = ((int64_t)(bh / H) * (H / group) + (bh % H) / group) * N * D;
     const T *Qh = Q + head;
-    const T *Kh = K + head;
-    const T *Vh = V + head;
+    const T *Kh = K + kv_head;
+    const T *Vh = V + kv_head;
 
     // state of the current query tile (set per tile below)
     int q0 = 0, qrow = 0, wq_lo = 0, wq_hi = 0, ntiles = 0;
@@ -443,41 +446,43 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
-                             int B, int H, int N, float scale, hipStream_t stream)
+                             int B, int H, int Hkv, int N, float scale, hipStream_t stream)
 {
     using C = FwdCfg<T, D>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const int64_t grid = (int64_t)B * H * (CAUSAL ? (nqt + 1) / 2 : nqt);
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, o, lse, N, nqt, scale);
+                       (const T *)q, (const T *)k, (const T *)v, o, lse, N, nqt, scale, H, H / Hkv);
     return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_fwd_c(const void *q, const void *k, const void *v, float *o, float *lse,
-                               int B, int H, int N, float scale, int causal, hipStream_t stream)
+                               int B, int H, int Hkv, int N, float scale, int causal,
+                               hipStream_t stream)
 {
-    return causal ? launch_fwd<T, D, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                  : launch_fwd<T, D, false>(q, k, v, o, lse, B, H, N, scale, stream);
+    return causal ? launch_fwd<T, D, true>(q, k, v, o, lse, B, H, Hkv, N, scale, stream)
+                  : launch_fwd<T, D, false>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
 }
 
 // Dispatch to the instantiation for (dtype, d, causal).  Arguments were
-// validated by the caller; dtype 0/1/2 = fp32/bf16/fp16, d in {64, 128}.
+// validated by the caller; dtype 0/1/2 = fp32/bf16/fp16, d in {64, 128},
+// Hkv divides H.
 hipError_t fwd_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
-                        int H, int N, int d, float scale, int causal, int dtype,
+                        int H, int Hkv, int N, int d, float scale, int causal, int dtype,
                         hipStream_t stream)
 {
     switch (dtype) {
     case 0:
-        return d == 64 ? launch_fwd_c<float, 64>(q, k, v, o, lse, B, H, N, scale, causal, stream)
-                       : launch_fwd_c<float, 128>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+        return d == 64 ? launch_fwd_c<float, 64>(q, k, v, o, lse, B, H, Hkv, N, scale, causal, stream)
+                       : launch_fwd_c<float, 128>(q, k, v, o, lse, B, H, Hkv, N, scale, causal, stream);
     case 1:
-        return d == 64 ? launch_fwd_c<__bf16, 64>(q, k, v, o, lse, B, H, N, scale, causal, stream)
-                       : launch_fwd_c<__bf16, 128>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+        return d == 64 ? launch_fwd_c<__bf16, 64>(q, k, v, o, lse, B, H, Hkv, N, scale, causal, stream)
+                       : launch_fwd_c<__bf16, 128>(q, k, v, o, lse, B, H, Hkv, N, scale, causal, stream);
     default:
         return d == 64
-                   ? launch_fwd_c<_Float16, 64>(q, k, v, o, lse, B, H, N, scale, causal, stream)
-                   : launch_fwd_c<_Float16, 128>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+                   ? launch_fwd_c<_Float16, 64>(q, k, v, o, lse, B, H, Hkv, N, scale, causal, stream)
+                   : launch_fwd_c<_Float16, 128>(q, k, v, o, lse, B, H, Hkv, N, scale, causal, stream);
     }
 }
 

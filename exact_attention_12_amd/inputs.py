@@ -33,6 +33,11 @@ class FwdConfig:
     causal: bool
     qk_factor: float = 1.0  # Q and K are drawn N(0,1) * qk_factor
     name: str = ""
+    Hkv: int = 0            # kv heads of K and V (0: H, i.e. multi-head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -57,6 +62,9 @@ FWD_CONFIGS = {
     4: FwdConfig(4, 1, 8, 65536, 128, torch.bfloat16, True, 2.0,
                  "B1 H8 N65536 d128 bf16 causal, Q,K x2"),
 }
+# grouped-query forward: config 3 with 8 kv heads (4 query heads per kv head)
+FWD_GQA_CONFIG = FwdConfig(7, 2, 32, 8192, 128, torch.bfloat16, True, 1.0,
+                           "B2 H32 Hkv8 N8192 d128 bf16 causal", Hkv=8)
 
 
 def normal(seed: int, shape, factor: float = 1.0, dtype=torch.float32) -> torch.Tensor:
@@ -68,12 +76,13 @@ def normal(seed: int, shape, factor: float = 1.0, dtype=torch.float32) -> torch.
 
 
 def fwd_inputs(cfg: FwdConfig):
-    """(q, k, v) CPU tensors [B, H, N, d] of cfg.dtype."""
+    """(q, k, v) CPU tensors of cfg.dtype: q [B, H, N, d], k and v [B, Hkv, N, d]."""
     shape = (cfg.B, cfg.H, cfg.N, cfg.d)
+    kv_shape = (cfg.B, cfg.kv_heads, cfg.N, cfg.d)
     base = 1000 * cfg.cid
     q = normal(base + 0, shape, cfg.qk_factor, cfg.dtype)
-    k = normal(base + 1, shape, cfg.qk_factor, cfg.dtype)
-    v = normal(base + 2, shape, 1.0, cfg.dtype)
+    k = normal(base + 1, kv_shape, cfg.qk_factor, cfg.dtype)
+    v = normal(base + 2, kv_shape, 1.0, cfg.dtype)
     return q, k, v
 
 

@@ -87,6 +87,23 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
            int d, float scale, int causal, int dtype, void *stream);
 
 /*
+ * fa_fwd_gqa -- fa_fwd with grouped-query heads: k and v have Hkv heads
+ * that H / Hkv consecutive query heads share (the num_kv_heads of the paged
+ * cache in the PagedAttention walkthrough, data-sketchers.com wiki, section
+ * "Concepts", applied to the forward pass).
+ *
+ *   q       : [B, H, N, d];  k, v : [B, Hkv, N, d];  o : [B, H, N, d] fp32;
+ *             lse : [B, H, N] fp32.  Layout, alignment and dtype as fa_fwd.
+ *   Hkv     : >= 1 and divides H (else FA_ERR_INVALID_ARG).  Query head h
+ *             reads kv head h / (H / Hkv).  Hkv = H is fa_fwd; Hkv = 1 is
+ *             multi-query attention.
+ * Every other argument, the result for each query head and the error
+ * behaviour are those of fa_fwd.
+ */
+int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
+               int Hkv, int N, int d, float scale, int causal, int dtype, void *stream);
+
+/*
  * fa_paged_decode_workspace_size -- bytes of device workspace that
  * fa_paged_decode needs for these sizes: the per-partition partial results
  * O_p [S, H, P, head_size] fp32 plus m_p and l_p [S, H, P] fp32, where

@@ -59,7 +59,7 @@ def _load():
     lib = ctypes.CDLL(LIB)
     vp, i, d, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int64
     lib.oracle_widen.argtypes = [vp, i, i64, vp]
-    lib.oracle_attention.argtypes = [vp, vp, vp, i, i, i, i, i, d, i, vp, i64, vp, vp, i]
+    lib.oracle_attention.argtypes = [vp, vp, vp, i, i, i, i, i, i, d, i, vp, i64, vp, vp, i]
     lib.oracle_probs.argtypes = [vp, vp, i, i, i, i, i, d, i, vp]
     lib.oracle_tiled_fa1.argtypes = [vp, vp, vp, i, i, d, i, i, i, vp, vp]
     lib.oracle_tiled_fa2.argtypes = [vp, vp, vp, i, i, d, i, i, i, vp, vp]
@@ -111,16 +111,20 @@ def widen(x) -> np.ndarray:
 
 
 def attention(q, k, v, scale, causal, rows=None, nthreads=None):
-    """Dense attention on [B, H, N, d] inputs.
+    """Dense attention on q [B, H, N, d] and k, v [B, Hkv, N, d] (Hkv divides H;
+    query head h uses kv head h // (H // Hkv)).
 
     Returns (o [B, H, R, d], lse [B, H, R]) in fp64, R = len(rows) or N.
     """
     qt, code = _host(q)
     kt, c2 = _host(k)
     vt, c3 = _host(v)
-    if not (code == c2 == c3) or qt.shape != kt.shape or qt.shape != vt.shape or qt.dim() != 4:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape and dtype")
+    if not (code == c2 == c3) or qt.dim() != 4 or kt.shape != vt.shape or kt.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k, v one [B, Hkv, N, d] shape, one dtype")
     B, H, N, d = qt.shape
+    Hkv = kt.shape[1]
+    if (kt.shape[0], kt.shape[2], kt.shape[3]) != (B, N, d) or H % Hkv != 0:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
     if rows is None:
         rarr, R = None, N
     else:
@@ -128,7 +132,7 @@ def attention(q, k, v, scale, causal, rows=None, nthreads=None):
         R = len(rarr)
     o = np.empty((B, H, R, d), dtype=np.float64)
     lse = np.empty((B, H, R), dtype=np.float64)
-    st = _load().oracle_attention(_p(qt), _p(kt), _p(vt), code, B, H, N, d, float(scale),
+    st = _load().oracle_attention(_p(qt), _p(kt), _p(vt), code, B, H, Hkv, N, d, float(scale),
                                   int(bool(causal)),
                                   None if rarr is None else _p(rarr), R, _p(o), _p(lse),
                                   nthreads or default_threads())

@@ -210,7 +210,7 @@ static double or_softmax_row(double *s, int64_t n, int d, or_value_fn vfn, const
 typedef struct {
     const void *q, *k, *v;
     int dtype;
-    int B, H, N, d;
+    int B, H, Hkv, N, d;
     double scale;
     int causal;
     const int64_t *rows;
@@ -238,40 +238,47 @@ static void or_fwd_item(void *vctx, int64_t item, double *s)
     int64_t r = item % x->nrows;
     int64_t bh = item / x->nrows;
     int64_t i = x->rows ? x->rows[r] : r;
-    int64_t base = bh * (int64_t)x->N * x->d; /* [B,H,N,d] contiguous */
+    int64_t base = bh * (int64_t)x->N * x->d; /* Q: [B,H,N,d] contiguous */
+    /* K, V: [B,Hkv,N,d]; query head h reads kv head h / (H / Hkv) */
+    int64_t b = bh / x->H, h = bh % x->H;
+    int64_t kvbase = (b * x->Hkv + h / (x->H / x->Hkv)) * (int64_t)x->N * x->d;
     /* admissible keys A_i = { j < N : not causal or j <= i } */
     int64_t n = x->causal ? (i + 1 < x->N ? i + 1 : x->N) : x->N;
     for (int64_t j = 0; j < n; ++j) {
         double dot = 0.0;
         for (int c = 0; c < x->d; ++c)
             dot += or_load(x->q, x->dtype, base + i * x->d + c) *
-                   or_load(x->k, x->dtype, base + j * x->d + c);
+                   or_load(x->k, x->dtype, kvbase + j * x->d + c);
         s[j] = x->scale * dot;
     }
-    or_dense_v dv = { x->v, x->dtype, base, x->d };
+    or_dense_v dv = { x->v, x->dtype, kvbase, x->d };
     double *o = x->o + item * x->d;
     x->lse[item] = or_softmax_row(s, n, x->d, or_dense_value, &dv, o);
 }
 
 /*
  * O = softmax(scale * Q K^T [+ causal mask]) V for every (b, h) and every
- * selected query row, with Q, K, V laid out [B, H, N, d] contiguous.
+ * selected query row, with Q laid out [B, H, N, d] and K, V [B, Hkv, N, d]
+ * contiguous; query head h attends with kv head h / (H / Hkv) (Hkv = H:
+ * multi-head attention; grouped query heads as in the num_kv_heads of
+ * [PA] "Concepts").
  *   rows  : query indices to evaluate (the same for every (b, h)); NULL
  *           means all N rows, in order.
  *   o     : [B, H, nrows, d] fp64;  lse : [B, H, nrows] fp64.
  * Returns 0, or -1 on a bad argument or allocation failure.
  */
-int oracle_attention(const void *q, const void *k, const void *v, int dtype, int B, int H, int N,
-                     int d, double scale, int causal, const int64_t *rows, int64_t nrows,
+int oracle_attention(const void *q, const void *k, const void *v, int dtype, int B, int H, int Hkv,
+                     int N, int d, double scale, int causal, const int64_t *rows, int64_t nrows,
                      double *o, double *lse, int nthreads)
 {
     if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || N < 1 || d < 1) return -1;
+    if (Hkv < 1 || H % Hkv != 0) return -1;
     if (or_elem_bytes(dtype) == 0) return -1;
     if (!rows) nrows = N;
     if (nrows < 1) return -1;
     for (int64_t r = 0; rows && r < nrows; ++r)
         if (rows[r] < 0 || rows[r] >= N) return -1;
-    or_fwd_ctx ctx = { q, k, v, dtype, B, H, N, d, scale, causal, rows, nrows, o, lse };
+    or_fwd_ctx ctx = { q, k, v, dtype, B, H, Hkv, N, d, scale, causal, rows, nrows, o, lse };
     return or_parallel(or_fwd_item, &ctx, (int64_t)B * H * nrows, N, nthreads);
 }
 

@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_exports_every_declared_function(fa_lib):
     names = declared_functions()
-    assert names == ["fa_fwd", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror"]
+    assert names == ["fa_fwd", "fa_fwd_gqa", "fa_paged_decode", "fa_paged_decode_workspace_size",
+                     "fa_strerror"]
     for n in names:
         assert hasattr(fa_lib, n), n
 
@@ -78,6 +79,25 @@ def test_fwd_validation(fa_lib):
     assert fwd(fa_lib, B=1 << 16, H=1 << 16, N=1 << 10, **base) == UNSUPPORTED
     # one head beyond 2 GiB (32-bit buffer offsets)
     assert fwd(fa_lib, N=1 << 23, d=128, dtype=1, o=P + (1 << 40), lse=P + (1 << 41)) == UNSUPPORTED
+
+
+def fwd_gqa(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=8, Hkv=2, N=16, d=64, scale=0.125, causal=0,
+            dtype=1):
+    return lib.fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype, None)
+
+
+def test_fwd_gqa_validation(fa_lib):
+    far, far2 = P + (1 << 30), P + (1 << 31)
+    base = dict(o=far, lse=far2)
+    assert fwd_gqa(fa_lib, Hkv=3, **base) == INVALID   # 8 % 3 != 0
+    assert fwd_gqa(fa_lib, Hkv=0, **base) == INVALID
+    assert fwd_gqa(fa_lib, Hkv=-2, **base) == INVALID
+    assert fwd_gqa(fa_lib, k=0, **base) == INVALID
+    assert fwd_gqa(fa_lib, d=96, **base) == UNSUPPORTED
+    assert fwd_gqa(fa_lib, v=P + 4, **base) == ALIGN
+    # o overlapping k, whose size is B * Hkv * N * d elements
+    kv = P + (1 << 28)
+    assert fwd_gqa(fa_lib, k=kv, o=kv + 16 * 64 * 2 * 2 - 16, lse=far2) == INVALID
 
 
 def dec(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=P, S=4, H=8, Hkv=8, D=128, BS=16, MB=4,

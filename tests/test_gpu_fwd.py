@@ -53,6 +53,21 @@ def test_config2_bf16(gpu, fa_lib, N):
     check_cfg(inputs.FWD_CONFIGS[2].replace(N=N), gpu)
 
 
+@pytest.mark.parametrize("dt,d,H,Hkv,causal", [
+    ("bf16", 128, 8, 2, True), ("bf16", 128, 8, 1, False), ("f16", 64, 6, 3, True),
+    ("f32", 64, 4, 2, False), ("f32", 128, 4, 1, True)])
+def test_grouped_kv_heads(gpu, fa_lib, dt, d, H, Hkv, causal):
+    dtype = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
+    cfg = inputs.FwdConfig(96, 2, H, 333, d, dtype, causal, 1.0, "gqa %s d%d H%d Hkv%d" % (dt, d, H, Hkv),
+                           Hkv=Hkv)
+    check_cfg(cfg, gpu)
+
+
+def test_gqa_headline_sampled_rows(gpu, fa_lib):
+    cfg = inputs.FWD_GQA_CONFIG
+    check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
+
+
 def test_config3_headline_sampled_rows(gpu, fa_lib):
     cfg = inputs.FWD_CONFIGS[3]
     check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))

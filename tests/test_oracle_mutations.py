@@ -28,7 +28,7 @@ MUTATIONS = [
      "s[j] = x->scale * dot;",
      "s[j] = dot;"),
     ("scores_use_q_twice",
-     "or_load(x->k, x->dtype, base + j * x->d + c)",
+     "or_load(x->k, x->dtype, kvbase + j * x->d + c)",
      "or_load(x->q, x->dtype, base + j * x->d + c)"),
     ("max_not_subtracted_in_lse",
      "    return m + log(l);\n}",
@@ -51,6 +51,9 @@ MUTATIONS = [
     ("tiled_fa2_rescale_sign",
      "double alpha = exp(m - mnew);",
      "double alpha = exp(mnew - m);"),
+    ("dense_kv_head_mapping",
+     "int64_t kvbase = (b * x->Hkv + h / (x->H / x->Hkv)) * (int64_t)x->N * x->d;",
+     "int64_t kvbase = (b * x->Hkv + h % x->Hkv) * (int64_t)x->N * x->d;"),
     ("decode_kv_head_mapping",
      "int kvh = h / (x->H / x->Hkv);",
      "int kvh = h % x->Hkv;"),

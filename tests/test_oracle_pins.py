@@ -211,6 +211,28 @@ def test_P9_causal_is_not_permutation_invariant():
     assert not np.allclose(oc[0, 0, : N - 1], on[0, 0, : N - 1])
 
 
+@pytest.mark.parametrize("Hkv", [1, 2])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_kv_heads_equal_repeated_kv(Hkv, causal):
+    # grouped query heads (k, v with Hkv heads) are multi-head attention on
+    # k, v repeated so that query head h sees kv head h // (H // Hkv)
+    B, H, N, d = 2, 4, 9, 5
+    q = t64(rnd(41, (B, H, N, d)))
+    k = t64(rnd(42, (B, Hkv, N, d)))
+    v = t64(rnd(43, (B, Hkv, N, d)))
+    o, lse = oracle.attention(q, k, v, 0.4, causal)
+    kr = torch.repeat_interleave(k, H // Hkv, dim=1)
+    vr = torch.repeat_interleave(v, H // Hkv, dim=1)
+    o2, lse2 = oracle.attention(q, kr, vr, 0.4, causal)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    # query heads of one group with equal queries give equal rows
+    q2 = q.clone()
+    q2[:, 1] = q2[:, 0]
+    o3, _ = oracle.attention(q2, k, v, 0.4, causal)
+    if Hkv == 1 or H // Hkv >= 2:
+        assert np.array_equal(o3[:, 0], o3[:, 1])
+
+
 def test_P12_single_token():
     q, k, v = rnd(27, (3, 2, 1, 16)), rnd(28, (3, 2, 1, 16)), rnd(29, (3, 2, 1, 16))
     for causal in (False, True):
