@@ -15,6 +15,8 @@ Functions (each cites the page passages it follows in ``oracle.c``):
   tiled_fa1 / tiled_fa2(q, k, v, scale, causal, Br, Bc)
                                                       the online recurrence in
                                                       both loop orders
+  attention_bwd(q, k, v, dout, scale, causal, rows=None, keys=None)
+                                                      gradients dQ, dK, dV
   paged_decode(...), paged_decode_partitioned(...)    single-query decode
   widen(x)                                            exact fp64 view
 """
@@ -66,8 +68,11 @@ def _load():
     lib.oracle_paged_decode.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, d, vp, vp, i]
     lib.oracle_paged_decode_partitioned.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, d, i,
                                                     vp, vp, vp, vp, vp, i]
+    lib.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, d, i, vp, i64, vp, i64,
+                                         vp, vp, vp, vp, i]
     for name in ("oracle_widen", "oracle_attention", "oracle_probs", "oracle_tiled_fa1",
-                 "oracle_tiled_fa2", "oracle_paged_decode", "oracle_paged_decode_partitioned"):
+                 "oracle_tiled_fa2", "oracle_paged_decode", "oracle_paged_decode_partitioned",
+                 "oracle_attention_bwd"):
         getattr(lib, name).restype = i
     _lib = lib
     return lib
@@ -138,6 +143,53 @@ def attention(q, k, v, scale, causal, rows=None, nthreads=None):
                                   nthreads or default_threads())
     _check(st, "oracle_attention")
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, scale, causal, rows=None, keys=None, nthreads=None):
+    """Gradients of dense attention for upstream gradient dout [B, H, N, d].
+
+    q, dout [B, H, N, d]; k, v [B, Hkv, N, d] (one storage dtype).  rows
+    selects the query rows whose dQ is returned (None: all N; an empty list
+    skips dQ), keys the key rows whose dK, dV are returned (None: all N).
+
+    Returns dict(dq [B, H, R, d], dk [B, Hkv, K, d], dv [B, Hkv, K, d],
+    D [B, H, N]) in fp64; D_i = sum_j P_ij dP_ij, NaN where no pass needed
+    row i.
+    """
+    qt, code = _host(q)
+    kt, c2 = _host(k)
+    vt, c3 = _host(v)
+    dt, c4 = _host(dout)
+    if not (code == c2 == c3 == c4) or qt.dim() != 4 or kt.dim() != 4:
+        raise ValueError("q, dout [B, H, N, d] and k, v [B, Hkv, N, d] of one dtype")
+    if dt.shape != qt.shape or kt.shape != vt.shape:
+        raise ValueError("dout must match q and v must match k")
+    B, H, N, d = qt.shape
+    Hkv = kt.shape[1]
+    if (kt.shape[0], kt.shape[2], kt.shape[3]) != (B, N, d) or H % Hkv != 0:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
+
+    def sel(x):
+        if x is None:
+            return None, N
+        a = np.ascontiguousarray(np.asarray(x, dtype=np.int64).reshape(-1))
+        return a, len(a)
+
+    rarr, R = sel(rows)
+    karr, K = sel(keys)
+    dq = np.empty((B, H, R, d), dtype=np.float64)
+    dk = np.empty((B, Hkv, K, d), dtype=np.float64)
+    dv = np.empty((B, Hkv, K, d), dtype=np.float64)
+    D = np.full((B, H, N), np.nan, dtype=np.float64)
+    dummy = np.empty(1, dtype=np.int64)
+    st = _load().oracle_attention_bwd(
+        _p(qt), _p(kt), _p(vt), _p(dt), code, B, H, Hkv, N, d, float(scale), int(bool(causal)),
+        None if rarr is None else _p(rarr if R else dummy), R,
+        None if karr is None else _p(karr if K else dummy), K,
+        _p(dq) if R else None, _p(dk) if K else None, _p(dv) if K else None, _p(D),
+        nthreads or default_threads())
+    _check(st, "oracle_attention_bwd")
+    return dict(dq=dq, dk=dk, dv=dv, D=D)
 
 
 def probs(q, k, scale, causal):

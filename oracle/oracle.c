@@ -662,3 +662,190 @@ int oracle_paged_decode_partitioned(const void *q, const void *k_cache, const vo
     return or_parallel(or_dec_item, &x, (int64_t)num_seqs * num_heads,
                        (int64_t)part_tokens + head_size, nthreads);
 }
+
+/* ------------------------------------------------------------------ */
+/* Dense attention backward                                             */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Gradients of O = softmax(scale * Q K^T [+ causal mask]) V given the
+ * upstream gradient dO = dL/dO.  The pages fix the method ([YJ] 7.1-7.2:
+ * the backward pass needs P, and FlashAttention recomputes it from Q, K, V
+ * and the saved row statistics instead of storing it); the gradients
+ * themselves are the chain rule applied to the forward definition:
+ *     P_ij  = exp(s_ij - m_i) / l_i               (row i of the forward)
+ *     dV_j  = sum_i P_ij dO_i
+ *     dP_ij = dO_i . V_j
+ *     D_i   = sum_j P_ij dP_ij                     (= dO_i . O_i)
+ *     dS_ij = P_ij (dP_ij - D_i)                   (softmax Jacobian)
+ *     dQ_i  = scale sum_j dS_ij K_j
+ *     dK_j  = scale sum_i dS_ij Q_i
+ * sums over admissible pairs only.  With grouped kv heads, dK and dV of kv
+ * head g collect the terms of every query head that reads g, query heads in
+ * ascending order.
+ *
+ * Two passes, each summing in ascending index order (so the result does not
+ * depend on the thread count):
+ *   1. per query row (b, h, i): m_i, l_i, D_i and, for selected rows, dQ_i;
+ *   2. per key row (b, g, j): dV_j and dK_j over query heads h of group g,
+ *      then rows i, recomputing P_ij and dP_ij with pass 1's m_i, l_i, D_i.
+ */
+typedef struct {
+    const void *q, *k, *v, *dout;
+    int dtype;
+    int B, H, Hkv, N, d;
+    double scale;
+    int causal;
+    const int64_t *rows, *keys;
+    int64_t nrows, nkeys;
+    const unsigned char *need_row; /* [N]: row i is needed by pass 1 */
+    double *m, *l, *D;             /* [B, H, N] row statistics */
+    double *dq, *dk, *dv;
+} or_bwd_ctx;
+
+static int64_t or_bwd_qbase(const or_bwd_ctx *x, int64_t b, int64_t h)
+{
+    return (b * x->H + h) * (int64_t)x->N * x->d;
+}
+
+static int64_t or_bwd_kvbase(const or_bwd_ctx *x, int64_t b, int64_t h)
+{
+    return (b * x->Hkv + h / (x->H / x->Hkv)) * (int64_t)x->N * x->d;
+}
+
+static double or_dot(const void *a, int64_t ia, const void *b, int64_t ib, int dtype, int d)
+{
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) acc += or_load(a, dtype, ia + c) * or_load(b, dtype, ib + c);
+    return acc;
+}
+
+/* pass 1, item = (b, h, r): r indexes all N rows */
+static void or_bwd_row_item(void *vctx, int64_t item, double *s)
+{
+    const or_bwd_ctx *x = (const or_bwd_ctx *)vctx;
+    const int64_t N = x->N, d = x->d;
+    int64_t i = item % N, bh = item / N;
+    int64_t b = bh / x->H, h = bh % x->H;
+    if (!x->need_row[i]) return;
+    int64_t qb = or_bwd_qbase(x, b, h), kb = or_bwd_kvbase(x, b, h);
+    int64_t n = x->causal ? i + 1 : N;
+    double *dp = s + N;
+    for (int64_t j = 0; j < n; ++j) s[j] = x->scale * or_dot(x->q, qb + i * d, x->k, kb + j * d, x->dtype, x->d);
+    double m = s[0];
+    for (int64_t j = 1; j < n; ++j)
+        if (s[j] > m) m = s[j];
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) l += exp(s[j] - m);
+    double D = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - m) / l; /* P_ij */
+        dp[j] = or_dot(x->dout, qb + i * d, x->v, kb + j * d, x->dtype, x->d);
+        D += s[j] * dp[j];
+    }
+    x->m[item] = m;
+    x->l[item] = l;
+    x->D[item] = D;
+    if (!x->dq) return;
+    int64_t r = -1;
+    if (!x->rows) r = i;
+    else
+        for (int64_t t = 0; t < x->nrows; ++t)
+            if (x->rows[t] == i) { r = t; break; }
+    if (r < 0) return;
+    double *dq = x->dq + (bh * x->nrows + r) * d;
+    for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < n; ++j)
+            acc += s[j] * (dp[j] - D) * or_load(x->k, x->dtype, kb + j * d + c);
+        dq[c] = x->scale * acc;
+    }
+}
+
+/* pass 2, item = (b, g, t): t indexes the selected keys */
+static void or_bwd_key_item(void *vctx, int64_t item, double *scratch)
+{
+    const or_bwd_ctx *x = (const or_bwd_ctx *)vctx;
+    const int64_t N = x->N, d = x->d;
+    int64_t t = item % x->nkeys, bg = item / x->nkeys;
+    int64_t b = bg / x->Hkv, g = bg % x->Hkv;
+    int64_t j = x->keys ? x->keys[t] : t;
+    int group = x->H / x->Hkv;
+    double *dk = x->dk + item * d, *dv = x->dv + item * d;
+    (void)scratch;
+    for (int c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
+    for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+        int64_t qb = or_bwd_qbase(x, b, h), kb = or_bwd_kvbase(x, b, h);
+        int64_t st = (b * x->H + h) * N;
+        for (int64_t i = x->causal ? j : 0; i < N; ++i) {
+            double sij = x->scale * or_dot(x->q, qb + i * d, x->k, kb + j * d, x->dtype, x->d);
+            double p = exp(sij - x->m[st + i]) / x->l[st + i];
+            double dp = or_dot(x->dout, qb + i * d, x->v, kb + j * d, x->dtype, x->d);
+            double ds = p * (dp - x->D[st + i]);
+            for (int c = 0; c < d; ++c) {
+                dv[c] += p * or_load(x->dout, x->dtype, qb + i * d + c);
+                dk[c] += ds * or_load(x->q, x->dtype, qb + i * d + c);
+            }
+        }
+    }
+    for (int c = 0; c < d; ++c) dk[c] *= x->scale;
+}
+
+/*
+ * q, dout [B, H, N, d]; k, v [B, Hkv, N, d] (contiguous, storage dtype).
+ *   rows  : query rows whose dQ is wanted (NULL: all N, in order; nrows may
+ *           be 0 with dq NULL to skip dQ);  dq [B, H, nrows, d] fp64.
+ *   keys  : key rows whose dK, dV are wanted (NULL: all N; nkeys 0 with
+ *           dk, dv NULL skips them);  dk, dv [B, Hkv, nkeys, d] fp64.
+ *   D     : optional [B, H, N] fp64 output of D_i (computed for every row
+ *           that pass 2 or dQ needs; other entries untouched).
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_attention_bwd(const void *q, const void *k, const void *v, const void *dout, int dtype,
+                         int B, int H, int Hkv, int N, int d, double scale, int causal,
+                         const int64_t *rows, int64_t nrows, const int64_t *keys, int64_t nkeys,
+                         double *dq, double *dk, double *dv, double *D_out, int nthreads)
+{
+    if (!q || !k || !v || !dout || B < 1 || H < 1 || N < 1 || d < 1) return -1;
+    if (Hkv < 1 || H % Hkv != 0) return -1;
+    if (or_elem_bytes(dtype) == 0) return -1;
+    if (!rows) nrows = N;
+    if (!keys) nkeys = N;
+    if (nrows < 0 || nkeys < 0) return -1;
+    if ((nrows > 0 && !dq) || (nkeys > 0 && (!dk || !dv))) return -1;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= N) return -1;
+    for (int64_t t = 0; keys && t < nkeys; ++t)
+        if (keys[t] < 0 || keys[t] >= N) return -1;
+    int64_t nst = (int64_t)B * H * N;
+    unsigned char *need = (unsigned char *)calloc((size_t)N, 1);
+    double *m = (double *)malloc(sizeof(double) * nst);
+    double *l = (double *)malloc(sizeof(double) * nst);
+    double *D = (double *)malloc(sizeof(double) * nst);
+    int rc = -1;
+    if (!need || !m || !l || !D) goto out;
+    /* pass 2 needs every row that sees a selected key; dQ needs its rows */
+    if (nkeys > 0) {
+        int64_t jmin = N;
+        for (int64_t t = 0; t < nkeys; ++t) {
+            int64_t j = keys ? keys[t] : t;
+            if (j < jmin) jmin = j;
+        }
+        for (int64_t i = causal ? jmin : 0; i < N; ++i) need[i] = 1;
+    }
+    for (int64_t r = 0; r < nrows; ++r) need[rows ? rows[r] : r] = 1;
+    {
+        or_bwd_ctx x = { q, k, v, dout, dtype, B, H, Hkv, N, d, scale, causal,
+                         rows, keys, nrows, nkeys, need, m, l, D,
+                         nrows > 0 ? dq : NULL, dk, dv };
+        rc = or_parallel(or_bwd_row_item, &x, nst, 2 * (int64_t)N, nthreads);
+        if (rc == 0 && nkeys > 0)
+            rc = or_parallel(or_bwd_key_item, &x, (int64_t)B * Hkv * nkeys, 0, nthreads);
+        if (rc == 0 && D_out)
+            for (int64_t it = 0; it < nst; ++it)
+                if (need[it % N]) D_out[it] = D[it];
+    }
+out:
+    free(need); free(m); free(l); free(D);
+    return rc;
+}

@@ -17,7 +17,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_decode.py",
-              "tests/test_oracle_tiling.py"]
+              "tests/test_oracle_tiling.py", "tests/test_oracle_bwd.py"]
 
 # (name, text in oracle.c, replacement); the text must occur in the source
 MUTATIONS = [
@@ -66,6 +66,36 @@ MUTATIONS = [
     ("merge_ignores_partition_sums",
      "double w = x->part_l[item * x->P + p] * exp(x->part_m[item * x->P + p] - m_all);",
      "double w = exp(x->part_m[item * x->P + p] - m_all);"),
+    ("bwd_dq_without_D",
+     "acc += s[j] * (dp[j] - D) * or_load(x->k, x->dtype, kb + j * d + c);",
+     "acc += s[j] * dp[j] * or_load(x->k, x->dtype, kb + j * d + c);"),
+    ("bwd_dk_without_D",
+     "double ds = p * (dp - x->D[st + i]);",
+     "double ds = p * dp;"),
+    ("bwd_dS_sign",
+     "double ds = p * (dp - x->D[st + i]);",
+     "double ds = p * (x->D[st + i] - dp);"),
+    ("bwd_D_unweighted",
+     "D += s[j] * dp[j];",
+     "D += dp[j];"),
+    ("bwd_dq_scale_dropped",
+     "dq[c] = x->scale * acc;",
+     "dq[c] = acc;"),
+    ("bwd_dk_scale_dropped",
+     "for (int c = 0; c < d; ++c) dk[c] *= x->scale;",
+     ""),
+    ("bwd_dv_reads_q",
+     "dv[c] += p * or_load(x->dout, x->dtype, qb + i * d + c);",
+     "dv[c] += p * or_load(x->q, x->dtype, qb + i * d + c);"),
+    ("bwd_dP_uses_keys",
+     "dp[j] = or_dot(x->dout, qb + i * d, x->v, kb + j * d, x->dtype, x->d);",
+     "dp[j] = or_dot(x->dout, qb + i * d, x->k, kb + j * d, x->dtype, x->d);"),
+    ("bwd_causal_skips_diagonal",
+     "for (int64_t i = x->causal ? j : 0; i < N; ++i) {",
+     "for (int64_t i = x->causal ? j + 1 : 0; i < N; ++i) {"),
+    ("bwd_group_mapping",
+     "for (int64_t h = g * group; h < (g + 1) * group; ++h) {",
+     "for (int64_t h = g; h < x->H; h += x->Hkv) {"),
 ]
 
 
