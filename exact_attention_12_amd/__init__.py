@@ -1,11 +1,13 @@
 """exact_attention_12_amd -- exact attention on AMD Instinct MI355X (gfx950).
 
 A thin ctypes binding over ``libfa.so`` (C ABI in ``include/fa.h``).  The
-functions named like the C entry points (``fa_fwd``, ``fa_paged_decode``,
+functions named like the C entry points (``fa_fwd``, ``fa_fwd_gqa``,
+``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_paged_decode``,
 ``fa_paged_decode_workspace_size``, ``fa_strerror``) only marshal arguments:
 every step of the computation runs in the library's HIP kernels.  PyTorch is
-used for device memory and streams.  ``forward`` and ``paged_decode`` are
-conveniences that allocate the outputs and call those entry points.
+used for device memory and streams.  ``forward``, ``backward`` and
+``paged_decode`` are conveniences that allocate the outputs and call those
+entry points.
 
 There is no fallback: if ``libfa.so`` is missing or fails to load, every call
 raises.
@@ -18,8 +20,9 @@ import torch
 
 __all__ = [
     "FA_F32", "FA_BF16", "FA_F16", "FA_DECODE_PARTITION_TOKENS", "FAError", "fa_fwd_gqa",
-    "fa_fwd", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror",
-    "forward", "paged_decode", "lib_path", "load_library",
+    "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
+    "fa_paged_decode_workspace_size", "fa_strerror", "forward", "backward", "paged_decode",
+    "lib_path", "load_library",
 ]
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
@@ -59,6 +62,10 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_gqa.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
     lib.fa_paged_decode_workspace_size.argtypes = [i, i, i, i]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
@@ -125,6 +132,31 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype=None, stre
         raise FAError(st, "fa_fwd_gqa")
 
 
+def fa_bwd_workspace_size(B, H, N) -> int:
+    """C entry point ``fa_bwd_workspace_size`` (bytes; 0 if invalid)."""
+    return int(load_library().fa_bwd_workspace_size(int(B), int(H), int(N)))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace,
+           workspace_bytes=None, dtype=None, stream=None):
+    """C entry point ``fa_bwd``: enqueue the backward pass on ``stream``.
+
+    q, dout [B, H, N, d] and k, v [B, Hkv, N, d] of one 16-bit element type;
+    o [B, H, N, d] and lse [B, H, N] fp32 from the forward pass; dq, dk, dv
+    fp32 outputs shaped like q, k, v.
+    """
+    if dtype is None:
+        dtype = _dtype_code(q.dtype)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().fa_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        int(B), int(H), int(Hkv), int(N), int(d), float(scale), int(bool(causal)), int(dtype),
+        _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_bwd")
+
+
 def fa_paged_decode_workspace_size(num_seqs, num_heads, head_size, max_context_len) -> int:
     """C entry point ``fa_paged_decode_workspace_size`` (bytes; 0 if invalid)."""
     return int(load_library().fa_paged_decode_workspace_size(
@@ -181,6 +213,34 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     else:
         fa_fwd_gqa(q, k, v, out, lse, B, H, Hkv, N, d, scale, causal, stream=stream)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):
+    """Allocate dq, dk, dv (fp32) and the workspace and run ``fa_bwd``;
+    returns (dq, dk, dv).  o and lse are ``forward``'s outputs."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("o", o, torch.float32)
+    _check_dev("lse", lse, torch.float32)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or dout.shape != q.shape:
+        raise ValueError("q, dout must be [B, H, N, d] and k, v one [B, Hkv, N, d] shape")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d) or H % Hkv != 0:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
+    if o.shape != q.shape or lse.shape != (B, H, N):
+        raise ValueError("o must be [B, H, N, d] and lse [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_size(B, H, N), 256), dtype=torch.uint8,
+                                device=q.device)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace,
+           stream=stream)
+    return dq, dk, dv
 
 
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,

@@ -19,6 +19,11 @@ hipError_t decode_dispatch(const void *q, const void *kc, const void *vc, const 
                            int max_ctx, float scale, int dtype, void *workspace,
                            hipStream_t stream);
 size_t decode_workspace_bytes(int num_seqs, int num_heads, int max_context_len);
+hipError_t bwd_dispatch(const void *q, const void *k, const void *v, const float *o,
+                        const float *lse, const void *dout, float *dq, float *dk, float *dv, int B,
+                        int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+                        void *workspace, hipStream_t stream);
+size_t bwd_workspace_bytes(int B, int H, int N);
 }  // namespace fa
 
 namespace {
@@ -96,6 +101,52 @@ extern "C" int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o,
                           void *stream)
 {
     return fwd_checked(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype, stream);
+}
+
+extern "C" size_t fa_bwd_workspace_size(int B, int H, int N)
+{
+    if (B < 1 || H < 1 || N < 1) return 0;
+    return fa::bwd_workspace_bytes(B, H, N);
+}
+
+extern "C" int fa_bwd(const void *q, const void *k, const void *v, const float *o,
+                      const float *lse, const void *dout, float *dq, float *dk, float *dv, int B,
+                      int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+    const int es = elem_bytes(dtype);
+    if (es == 0) return FA_ERR_INVALID_ARG;
+    if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const int64_t blocks = ((int64_t)N + kFwdRowsPerWorkgroup - 1) / kFwdRowsPerWorkgroup;
+    if ((int64_t)B * H * blocks > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)N * d * es > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(lse, 4))
+        return FA_ERR_ALIGNMENT;
+    const size_t need = fa::bwd_workspace_bytes(B, H, N);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return FA_ERR_ALIGNMENT;
+    const uint64_t rows = (uint64_t)B * H * N, kv_rows = (uint64_t)B * Hkv * N;
+    const void *ins[6] = {q, k, v, o, lse, dout};
+    const uint64_t in_bytes[6] = {rows * d * es, kv_rows * d * es, kv_rows * d * es,
+                                  rows * d * 4,  rows * 4,         rows * d * es};
+    void *outs[4] = {dq, dk, dv, workspace};
+    const uint64_t out_bytes[4] = {rows * d * 4, kv_rows * d * 4, kv_rows * d * 4, need};
+    for (int a = 0; a < 4; ++a) {
+        for (int i = 0; i < 6; ++i)
+            if (overlap(outs[a], out_bytes[a], ins[i], in_bytes[i])) return FA_ERR_INVALID_ARG;
+        for (int c = a + 1; c < 4; ++c)
+            if (overlap(outs[a], out_bytes[a], outs[c], out_bytes[c])) return FA_ERR_INVALID_ARG;
+    }
+    const hipError_t e = fa::bwd_dispatch(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale,
+                                          causal ? 1 : 0, dtype, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 extern "C" size_t fa_paged_decode_workspace_size(int num_seqs, int num_heads, int head_size,

@@ -36,16 +36,11 @@
 //  - causal: tiles entirely above the diagonal are never loaded; a wave skips
 //    the arithmetic of tiles that are fully masked for its 32 rows; only
 //    diagonal and ragged-tail tiles pay for element masks.
-#include "fa_device.h"
+#include "fa_tile.h"
 
 #include <type_traits>
 
-
 namespace fa {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 template <typename T, int D> struct FwdCfg {
     static constexpr int KW = Mma<T>::KW;
@@ -69,32 +64,6 @@ template <typename T, int D> struct FwdCfg {
     static_assert(NLD % 4 == 0, "tile loads must split evenly over the waves");
     static_assert(D % 32 == 0 && BC % 32 == 0, "tile shapes");
 };
-
-// Chunk swizzle: the 16-byte chunk c of LDS row r is stored at position
-// c ^ swz(r).  LDS serves a 16-byte read 16 lanes per pass and an 8-byte read
-// 32 lanes per pass, 64 banks of 4 bytes each.  The form below (found by
-// exhaustive search over XOR-of-shifted-row-bit forms under that model)
-// gives both read patterns the minimum number of passes: the K operand (16
-// consecutive rows, one chunk) and the V transpose read (4 rows x 4 chunks
-// per 32 lanes).  It depends on the row only through row % 16.
-template <int CPR, int ES> __device__ __forceinline__ int swz(int row)
-{
-    if constexpr (ES == 2)
-        return CPR >= 16 ? (((row & 3) << 2) ^ ((row >> 2) & 3)) : (((row & 3) << 1) ^ ((row >> 2) & 3));
-    else
-        return row & 15;
-}
-
-// Buffer resource word 3 for raw (unformatted, unswizzled) byte addressing.
-constexpr int kBufferFlags = 0x00020000;
-
-// 16 bytes per lane from buffer r at byte offset voff + soff into LDS at
-// lds + 16 * lane (the LDS base must be the same for the whole wave).
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char *lds, int voff,
-                                                  int soff)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
-}
 
 // Bound on the probabilities taken against a stale reference max (see the
 // softmax step in the kernel): 2^14, representable in every input type.

@@ -7,7 +7,8 @@ it produces.
 Recipe (every tensor on the host first, so both sides see identical values):
   seed = 1000 * config_id + t, with t = 0 for Q, 1 for K, 2 for V, 3 for the
   context lengths, 4 for the block permutation, 5 for sampled rows, 6 for the
-  decode query;
+  decode query, 7 for the upstream gradient dO of the backward pass, 8 for
+  sampled keys;
   numpy PCG64 ``standard_normal`` in fp32, times the config's factor, then one
   round-to-nearest-even cast to the element type (``torch.Tensor.to``).
 """
@@ -18,7 +19,7 @@ import numpy as np
 import torch
 
 __all__ = ["FwdConfig", "FWD_CONFIGS", "DecodeConfig", "DECODE_CONFIG", "normal",
-           "fwd_inputs", "sample_rows", "decode_inputs"]
+           "fwd_inputs", "bwd_dout", "sample_rows", "decode_inputs"]
 
 
 @dataclass(frozen=True)
@@ -50,7 +51,7 @@ class FwdConfig:
 
     def replace(self, **kw) -> "FwdConfig":
         args = dict(cid=self.cid, B=self.B, H=self.H, N=self.N, d=self.d, dtype=self.dtype,
-                    causal=self.causal, qk_factor=self.qk_factor, name=self.name)
+                    causal=self.causal, qk_factor=self.qk_factor, name=self.name, Hkv=self.Hkv)
         args.update(kw)
         return FwdConfig(**args)
 
@@ -84,6 +85,11 @@ def fwd_inputs(cfg: FwdConfig):
     k = normal(base + 1, kv_shape, cfg.qk_factor, cfg.dtype)
     v = normal(base + 2, kv_shape, 1.0, cfg.dtype)
     return q, k, v
+
+
+def bwd_dout(cfg: FwdConfig) -> torch.Tensor:
+    """Upstream gradient dO [B, H, N, d] of cfg.dtype, N(0,1); CPU tensor."""
+    return normal(1000 * cfg.cid + 7, (cfg.B, cfg.H, cfg.N, cfg.d), 1.0, cfg.dtype)
 
 
 def sample_rows(N: int, count: int = 256, seed: int = 5) -> np.ndarray:

@@ -12,7 +12,11 @@
  *     (FlashAttention-2 order); "Flash Attention" (suniverse77.github.io),
  *     Eq. (1)-(4).
  *
- *  2. fa_paged_decode: single-query attention of one new token per sequence
+ *  2. fa_bwd: the backward pass of fa_fwd / fa_fwd_gqa, dQ, dK, dV for an
+ *     upstream gradient dO, with the blocks of P recomputed on chip from Q,
+ *     K and the saved lse instead of being stored (youngju.dev section 7.2).
+ *
+ *  3. fa_paged_decode: single-query attention of one new token per sequence
  *     against its context stored in a paged (block-table) KV cache, split
  *     into context partitions whose partial results (m, l, O) are merged with
  *     Eq. (4) of "Flash Attention" generalised to P parts.  The cache layout
@@ -43,7 +47,7 @@
 extern "C" {
 #endif
 
-/* element type of q, k, v (fa_fwd) and of q, caches, out (fa_paged_decode) */
+/* element type of q, k, v (fa_fwd, fa_bwd) and of q, caches, out (fa_paged_decode) */
 typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype_t;
 
 /* status codes */
@@ -102,6 +106,49 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
  */
 int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
                int Hkv, int N, int d, float scale, int causal, int dtype, void *stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace that fa_bwd needs: two
+ * fp32 values per query row (D_i = dO_i . O_i and lse_i * log2 e),
+ * 2 * B * H * N * 4 bytes rounded up to 256.  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N);
+
+/*
+ * fa_bwd -- gradients of the attention forward pass (youngju.dev sections
+ * 7.1-7.3: S and P are not stored; each block of P is recomputed from Q, K
+ * and lse).  With s_ij = scale q_i . k_j and P_ij = exp(s_ij - lse_i) over
+ * the keys row i may see:
+ *     dV_j = sum_i P_ij dO_i,  dP_ij = dO_i . v_j,  D_i = dO_i . O_i,
+ *     dS_ij = P_ij (dP_ij - D_i),
+ *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
+ * the chain rule of the forward definition (dK, dV of a kv head sum over the
+ * query heads that read it).
+ *
+ *   q, dout : [B, H, N, d], element type `dtype`, 16-byte aligned.
+ *   k, v    : [B, Hkv, N, d], element type `dtype`, 16-byte aligned.
+ *   o, lse  : the forward pass's outputs for these q, k, v, scale and mask:
+ *             o [B, H, N, d] fp32 (16-byte aligned), lse [B, H, N] fp32
+ *             (4-byte aligned).  Read only.
+ *   dq      : [B, H, N, d] fp32, 16-byte aligned.  Written.
+ *   dk, dv  : [B, Hkv, N, d] fp32, 16-byte aligned.  Written.
+ *   Hkv     : >= 1 and divides H; query head h reads kv head h / (H / Hkv).
+ *   B, H, N, d, scale, causal : as fa_fwd (d 64 or 128).
+ *   dtype   : FA_BF16 or FA_F16 (FA_F32: FA_ERR_UNSUPPORTED).  Products are
+ *             exact and accumulate in fp32; P and dS are rounded to `dtype`
+ *             (round to nearest even) before the products dV = P^T dO,
+ *             dK = dS^T Q and dQ = dS K on the matrix cores.
+ *   workspace : device buffer of at least fa_bwd_workspace_size(B, H, N)
+ *             bytes, 256-byte aligned, overwritten by the call.  Concurrent
+ *             calls need separate workspaces.
+ *   stream  : hipStream_t or NULL.
+ * Inputs may alias each other; dq, dk, dv and workspace must not overlap
+ * one another or any input.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,
+           const void *dout, float *dq, float *dk, float *dv, int B, int H, int Hkv, int N, int d,
+           float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
+           void *stream);
 
 /*
  * fa_paged_decode_workspace_size -- bytes of device workspace that

@@ -15,6 +15,11 @@ TOL = {
     torch.float16: dict(o_max=1e-2, o_mean=1e-3, lse_max=1e-3),
 }
 DECODE_TOL = dict(o_max=1e-2, o_mean=1e-3)
+# Backward (16-bit inputs, fp32 outputs): per gradient tensor, the largest
+# error against the largest reference magnitude, and the mean error against
+# the mean reference magnitude, each with a small absolute floor for
+# gradients that are exactly zero in the reference (N = 1).
+BWD_TOL = dict(max_rel=2e-2, mean_rel=5e-3, floor=1e-5)
 
 
 _LOG = os.environ.get("FA_PROGRESS_LOG") or os.path.join(
@@ -52,3 +57,22 @@ def assert_fwd_close(o, lse, o_ref, lse_ref, dtype, label=""):
     assert omean <= tol["o_mean"], (label, omean)
     assert lmax <= tol["lse_max"], (label, lmax)
     return omax, omean, lmax
+
+
+def assert_bwd_close(dq, dk, dv, ref, dtype, label=""):
+    """dq, dk, dv: GPU gradients (numpy fp64) at the oracle's rows / keys."""
+    out = {}
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        r = ref[name]
+        if r.size == 0:
+            continue
+        assert np.all(np.isfinite(got)), "non-finite %s %s" % (name, label)
+        emax, emean = errors(got, r)
+        rmax, rmean = float(np.abs(r).max()), float(np.abs(r).mean())
+        out[name] = (emax, emean, rmax, rmean)
+        progress("%s %s max|err|=%.3g mean|err|=%.3g max|ref|=%.3g mean|ref|=%.3g" % (
+            label, name, emax, emean, rmax, rmean))
+    for name, (emax, emean, rmax, rmean) in out.items():
+        assert emax <= BWD_TOL["max_rel"] * rmax + BWD_TOL["floor"], (label, name, emax, rmax)
+        assert emean <= BWD_TOL["mean_rel"] * rmean + BWD_TOL["floor"], (label, name, emean, rmean)
+    return out

@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_exports_every_declared_function(fa_lib):
     names = declared_functions()
-    assert names == ["fa_fwd", "fa_fwd_gqa", "fa_paged_decode", "fa_paged_decode_workspace_size",
-                     "fa_strerror"]
+    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_gqa", "fa_paged_decode",
+                     "fa_paged_decode_workspace_size", "fa_strerror"]
     for n in names:
         assert hasattr(fa_lib, n), n
 
@@ -98,6 +98,53 @@ def test_fwd_gqa_validation(fa_lib):
     # o overlapping k, whose size is B * Hkv * N * d elements
     kv = P + (1 << 28)
     assert fwd_gqa(fa_lib, k=kv, o=kv + 16 * 64 * 2 * 2 - 16, lse=far2) == INVALID
+
+
+FAR = [P + (1 << s) for s in (30, 31, 32, 33)]  # four disjoint output regions
+
+
+def bwd(lib, q=P, k=P, v=P, o=P, lse=P, dout=P, dq=FAR[0], dk=FAR[1], dv=FAR[2], B=1, H=2, Hkv=1,
+        N=16, d=64, scale=0.125, causal=1, dtype=1, ws=FAR[3], wsb=1 << 20):
+    return lib.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype, ws,
+                      wsb, None)
+
+
+def test_bwd_validation(fa_lib):
+    assert bwd(fa_lib, q=0) == INVALID
+    assert bwd(fa_lib, dout=0) == INVALID
+    assert bwd(fa_lib, lse=0) == INVALID
+    assert bwd(fa_lib, dv=0) == INVALID
+    assert bwd(fa_lib, B=0) == INVALID
+    assert bwd(fa_lib, N=-1) == INVALID
+    assert bwd(fa_lib, Hkv=3) == INVALID          # 2 % 3 != 0
+    assert bwd(fa_lib, Hkv=0) == INVALID
+    assert bwd(fa_lib, scale=float("nan")) == INVALID
+    assert bwd(fa_lib, scale=-2.0) == INVALID
+    assert bwd(fa_lib, dtype=5) == INVALID
+    assert bwd(fa_lib, dtype=0) == UNSUPPORTED    # fp32 inputs
+    assert bwd(fa_lib, d=96) == UNSUPPORTED
+    assert bwd(fa_lib, B=1 << 16, H=1 << 16, Hkv=1, N=1 << 10, wsb=1 << 62) == UNSUPPORTED
+    assert bwd(fa_lib, N=1 << 23, d=128, wsb=1 << 40) == UNSUPPORTED  # one head > 2 GiB
+    assert bwd(fa_lib, dout=P + 8) == ALIGN
+    assert bwd(fa_lib, dq=FAR[0] + 4) == ALIGN
+    assert bwd(fa_lib, lse=P + 2) == ALIGN
+    assert bwd(fa_lib, ws=0) == WORKSPACE
+    assert bwd(fa_lib, wsb=64) == WORKSPACE
+    assert bwd(fa_lib, ws=FAR[3] + 16) == ALIGN
+    # outputs overlapping an input or one another
+    assert bwd(fa_lib, dq=P) == INVALID
+    assert bwd(fa_lib, dk=FAR[0] + 64) == INVALID
+    assert bwd(fa_lib, ws=FAR[2]) == INVALID
+    # dv overlapping o, whose size is B * H * N * d fp32 (o placed apart from q)
+    o = P + (1 << 28)
+    assert bwd(fa_lib, o=o, dv=o + 2 * 16 * 64 * 4 - 16) == INVALID
+
+
+def test_bwd_workspace_size(fa_lib):
+    assert fa.fa_bwd_workspace_size(2, 32, 8192) == 2 * 2 * 32 * 8192 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 3) == 256
+    assert fa.fa_bwd_workspace_size(0, 1, 3) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 0) == 0
 
 
 def dec(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=P, S=4, H=8, Hkv=8, D=128, BS=16, MB=4,
