@@ -9,7 +9,9 @@ One step = one pass of the whole path over one batch of synthetic input:
      a 20000-block pool addressed through a random permutation;
   3. fa_paged_decode on the grouped-query variant: the same shape with 8 kv
      heads (4 query heads per kv head);
-  4. fa_fwd_gqa on the forward workload with 8 kv heads (fwd_gqa).
+  4. fa_fwd_gqa on the forward workload with 8 kv heads (fwd_gqa);
+  5. fa_bwd on the forward workload (bwd): dQ, dK, dV for a seeded N(0,1)
+     upstream gradient, from step 1's o and lse.
 Inputs are generated on the host with fixed seeds and copied to HBM before
 the timed region.  The timed region runs K steps between two device
 synchronisations; each kernel call is bracketed by HIP events recorded on the
@@ -177,6 +179,13 @@ def main():
                       device=dev)
     del gdec["k_cache"], gdec["v_cache"]
 
+    log("generating the upstream gradient of the backward pass")
+    gdo = inputs.bwd_dout(fcfg).to(dev)
+    bdq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    bdk = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    bdv = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    bws = torch.empty(fa.fa_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
+
     stream = torch.cuda.current_stream()
 
     def step(evs=None):
@@ -196,13 +205,17 @@ def main():
         fa.fa_fwd_gqa(gfq, gfk, gfv, go, glse, B, H, gHkv_f, N, d, fscale, True, stream=stream)
         if evs:
             evs[4].record(stream)
+        fa.fa_bwd(qd, kd, vd, o, lse, gdo, bdq, bdk, bdv, B, H, H, N, d, fscale, True, bws,
+                  stream=stream)
+        if evs:
+            evs[5].record(stream)
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -218,10 +231,17 @@ def main():
     gqa_avg = sum(gqa_ms) / len(gqa_ms)
     fgqa_ms = [e[3].elapsed_time(e[4]) for e in evs]
     fgqa_avg = sum(fgqa_ms) / len(fgqa_ms)
+    bwd_ms = [e[4].elapsed_time(e[5]) for e in evs]
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    # backward flop: five N x N x d products per head (S recomputed, dP, dV,
+    # dK, dQ), 2.5 times the forward's two
+    bwd_flops = 2.5 * fcfg.flops()
+    bwd_tflops = bwd_flops / (bwd_avg * 1e-3) / 1e12
 
     # quick sanity of the last step's results (full parity lives in the tests)
     finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item()
-                  and torch.isfinite(gout).all().item() and torch.isfinite(go).all().item())
+                  and torch.isfinite(gout).all().item() and torch.isfinite(go).all().item()
+                  and all(torch.isfinite(t).all().item() for t in (bdq, bdk, bdv)))
 
     flops = fcfg.flops()
     tflops = flops / (fwd_avg * 1e-3) / 1e12
@@ -290,6 +310,16 @@ def main():
                                  "frac": round(qcfg.flops() / (fgqa_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                  "kernel": "fa_fwd_kernel<bf16,128,causal> (grouped kv heads)",
                                  "algorithmic_per_launch": qcfg.flops()}},
+        "bwd": {"metric": "attention backward TFLOP/s (dQ, dK, dV; 5 products of 2*N^2*d "
+                          "per head, halved for causal)",
+                "value": round(bwd_tflops, 2), "unit": "TFLOP/s", "workload": fcfg.name,
+                "ms_avg": round(bwd_avg, 4), "ms_min": round(min(bwd_ms), 4),
+                "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                             "kernel": "fa_bwd_prep_kernel + fa_bwd_dkdv_kernel + fa_bwd_dq_kernel "
+                                       "(bf16, d=128, causal)",
+                             "algorithmic_per_launch": bwd_flops}},
         "decode_gqa": {"metric": "paged decode HBM bandwidth, 4 query heads per kv head",
                        "value": round(gqa_gbs, 1), "unit": "GB/s",
                        "workload": gcfg.name, "sum_ctx": int(gctx.sum()),

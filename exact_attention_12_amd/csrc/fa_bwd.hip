@@ -17,18 +17,24 @@
 //  1. prep: D_i = dO_i . O_i and lse_i * log2(e) per query row;
 //  2. dK/dV: one workgroup of 4 waves per (b, kv head, 128-key block), 32
 //     keys per wave.  Each wave keeps its K and V rows in registers as
-//     matrix-core operands and its dK^T, dV^T accumulators in registers; the
-//     Q and dO tiles (64 rows) of every query head that reads this kv head
-//     stream through LDS, double buffered.  Per 32-query block:
+//     matrix-core operands and its dK^T, dV^T accumulators in registers
+//     (one wave per SIMD: that state alone takes 192 of its 512 registers);
+//     the Q and dO tiles (128 rows) of every query head that reads this kv
+//     head stream through LDS, double buffered.  Per 32-query block:
 //       S = Q K^T, dP = dO V^T        (lane = key, registers = queries)
 //       P, dS elementwise
 //       dV^T += dO^T P,  dK^T += Q^T dS   (P and dS feed the matrix core
 //                                          straight from the registers; the
 //                                          Q^T, dO^T operands come from the
 //                                          LDS transpose read)
+//     The four blocks of a tile run as a three-stage software pipeline:
+//     the products of S, dP for block n and of dV, dK for block n-2 are
+//     issued together, with the elementwise work of block n-1 spread over
+//     them, and every LDS operand is read two products ahead.  With a single
+//     wave per SIMD nothing else hides the vector work or the LDS latency;
 //  3. dQ: one workgroup of 4 waves per (b, h, 128-query tile), 32 queries per
 //     wave, the forward pass's layout: Q and dO rows in registers, K and V
-//     tiles (64 keys) streamed through LDS;
+//     tiles (64 keys) streamed through LDS, two waves per SIMD;
 //       S^T = K Q^T, dP^T = V dO^T    (lane = query, registers = keys)
 //       dQ^T += K^T dS^T.
 // Splitting dQ from dK/dV recomputes S and dP once more (7 matrix products
@@ -40,6 +46,7 @@
 
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 namespace fa {
 
@@ -69,35 +76,48 @@ template <typename T, int D> struct BwdCfg {
 // LDS row p / CPR, position p % CPR, which holds global chunk
 // (p % CPR) ^ swz(row).  Rows at or past the end of the sequence re-read row
 // N-1, so every LDS row holds finite values.
-template <class C> struct TileLoader {
-    int row[C::NLD_W], off[C::NLD_W];
+template <class C, int ROWS> struct TileLoader {
+    static constexpr int NLD_W = ROWS * C::CPR / kWave / 4;  // 1 KiB loads per wave
+    static_assert(ROWS * C::CPR % (4 * kWave) == 0, "tile loads must split evenly over the waves");
+    int row[NLD_W], off[NLD_W];
     __device__ __forceinline__ void init(int wave, int lane)
     {
 #pragma unroll
-        for (int i = 0; i < C::NLD_W; ++i) {
-            const int p = (wave * C::NLD_W + i) * kWave + lane;
+        for (int i = 0; i < NLD_W; ++i) {
+            const int p = (wave * NLD_W + i) * kWave + lane;
             row[i] = p / C::CPR;
             off[i] = (row[i] * (C::ROWB / C::ES) + ((p % C::CPR) ^ swz<C::CPR, C::ES>(row[i])) * C::VEC) * C::ES;
         }
     }
-    // tile of rows [r0, r0 + BT) of the buffer r into LDS at dst
+    // tile of rows [r0, r0 + ROWS) of the buffer r into LDS at dst
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char *dst, int wave, int r0, int N) const
     {
         const int soff = r0 * C::ROWB;
-        if (r0 + C::BT <= N) {
+        if (r0 + ROWS <= N) {
 #pragma unroll
-            for (int i = 0; i < C::NLD_W; ++i)
-                buffer_load_lds16(r, dst + (wave * C::NLD_W + i) * 1024, off[i], soff);
+            for (int i = 0; i < NLD_W; ++i)
+                buffer_load_lds16(r, dst + (wave * NLD_W + i) * 1024, off[i], soff);
         } else {
 #pragma unroll
-            for (int i = 0; i < C::NLD_W; ++i) {
+            for (int i = 0; i < NLD_W; ++i) {
                 const int over = r0 + row[i] - (N - 1);
-                buffer_load_lds16(r, dst + (wave * C::NLD_W + i) * 1024,
+                buffer_load_lds16(r, dst + (wave * NLD_W + i) * 1024,
                                   over > 0 ? off[i] - over * C::ROWB : off[i], soff);
             }
         }
     }
 };
+
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F &&f)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order
+template <int N, class F> __device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
 
 // byte offset of element e of row r in a swizzled tile
 template <class C> __device__ __forceinline__ int tile_off(int r, int e)
@@ -126,6 +146,16 @@ template <typename frag> __device__ __forceinline__ frag tr_read(const char *blk
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(blk + o0));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(blk + o1));
     return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// the 8 (or KW) registers [st*KW, st*KW + KW) of x, rounded into one operand
+template <typename T> __device__ __forceinline__ typename Mma<T>::frag pack_regs(const f32x16 &x, int st)
+{
+    constexpr int KW = Mma<T>::KW;
+    float t[KW];
+#pragma unroll
+    for (int e = 0; e < KW; ++e) t[e] = x[st * KW + e];
+    return Mma<T>::pack(t);
 }
 
 // Workgroup id with the XCD remap: consecutive ids are dispatched
@@ -175,6 +205,57 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const float *__restric
 // ---------------------------------------------------------------------------
 // 2. dK, dV
 // ---------------------------------------------------------------------------
+// Schedule of one full tile of the dK/dV kernel: NB 32-query blocks and NP
+// matrix pairs per block for S/dP and again for dV/dK.  Step s issues the
+// S/dP pairs of block s (s < NB) and the dV/dK pairs of block s-2 (s >= 2),
+// alternating when both are present; the elementwise work of block s-1
+// (1 <= s <= NB) is spread over the pairs of step s, so that every matrix
+// instruction has a share of it to hide.
+template <int NB, int NP> struct DkdvSched {
+    static constexpr int NSTEP = NB + 2;
+    static constexpr int NOPS = 2 * NB * NP;
+    static constexpr int nsdp(int s) { return s < NB ? NP : 0; }
+    static constexpr int ndvdk(int s) { return s >= 2 && s < NB + 2 ? NP : 0; }
+    static constexpr int nops(int s) { return nsdp(s) + ndvdk(s); }
+    static constexpr int first(int s)
+    {
+        int g = 0;
+        for (int i = 0; i < s; ++i) g += nops(i);
+        return g;
+    }
+    static constexpr int step_of(int g)
+    {
+        int s = 0;
+        while (g >= nops(s)) {
+            g -= nops(s);
+            ++s;
+        }
+        return s;
+    }
+    static constexpr bool both(int s) { return nsdp(s) > 0 && ndvdk(s) > 0; }
+    // 0: S/dP pair, 1: dV/dK pair
+    static constexpr int kind(int g)
+    {
+        const int s = step_of(g), k = g - first(s);
+        return both(s) ? (k & 1) : (nsdp(s) ? 0 : 1);
+    }
+    static constexpr int block(int g) { return kind(g) == 0 ? step_of(g) : step_of(g) - 2; }
+    static constexpr int pair(int g)
+    {
+        const int s = step_of(g), k = g - first(s);
+        return both(s) ? k / 2 : k;
+    }
+    // element e (0..15) of block b: with the pair at this index (step b+1,
+    // starting one pair in, so that the scores of block b have landed)
+    static constexpr int elem_op(int b, int e) { return first(b + 1) + 1 + e * (nops(b + 1) - 1) / 16; }
+    // statistics of 4-row group r of block b are read two pairs ahead
+    static constexpr int stats_op(int b, int r)
+    {
+        const int g = elem_op(b, 4 * r) - 2;
+        return g < 0 ? 0 : g;
+    }
+};
+
 template <typename T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
@@ -186,8 +267,14 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int KW = C::KW;
-    constexpr int STATB = C::BT * 4;                  // lse2 or D of one tile
-    constexpr int STAGEB = 2 * C::TILEB + 2 * STATB;  // Q, dO, lse2, D
+    constexpr int BQ = 128;                      // query rows per streamed tile
+    constexpr int NBQ = BQ / 32;                 // 32-query blocks per tile
+    constexpr int QTB = BQ * C::ROWB;            // bytes of a Q or dO tile
+    constexpr int STATB = BQ * 4;                // lse2 or D of one tile
+    constexpr int STAGEB = 2 * QTB + 2 * STATB;  // Q, dO, lse2, D
+    constexpr int NP = C::QK_STEPS;              // matrix pairs per block, S/dP and dV/dK alike
+    static_assert(C::PV_STEPS * C::DB == NP, "S/dP and dV/dK take the same number of pairs");
+    using S = DkdvSched<NBQ, NP>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
 
     const int tid = threadIdx.x;
@@ -207,7 +294,7 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
     const int64_t kv_head = (int64_t)bkv * N * D;
     const int head_bytes = N * C::ROWB;
 
-    TileLoader<C> ld;
+    TileLoader<C, BQ> ld;
     ld.init(wave, lane);
     int q_rd[C::QK_STEPS];  // row-fragment read: row col, elements st*2KW + h*KW
 #pragma unroll
@@ -216,7 +303,7 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
     tr_offsets<C>(lane, tr);
 
     const float c = fmaxf(scale * kLog2e, 1e-30f);
-    const int nqt = (N + C::BT - 1) / C::BT;
+    const int nqt = (N + BQ - 1) / BQ;
 
     for (int item = 0; item < (CAUSAL ? 2 : 1); ++item) {
         const int kt = CAUSAL ? (item == 0 ? pi : num_ktiles - 1 - pi) : pi;
@@ -243,7 +330,7 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
             dv[db] = f32x16{};
         }
         // query tiles that can see a key of this block
-        const int qt0 = CAUSAL ? (kt * C::BW) / C::BT : 0;
+        const int qt0 = CAUSAL ? (kt * C::BW) / BQ : 0;
 
         for (int t = 0; t < group; ++t) {
             const int64_t bh = (int64_t)b * H + (int64_t)g * group + t;
@@ -258,89 +345,168 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
 
             auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
                 char *qd = smem + buf * STAGEB;
-                ld.load(qrs, qd, wave, j * C::BT, N);
-                ld.load(ors, qd + C::TILEB, wave, j * C::BT, N);
-                // lse2 and D of rows j*BT + lane (rows past the end re-read N-1)
-                if (wave < 2) {
-                    const int voff = min(j * C::BT + lane, N - 1) * 4;
-                    buffer_load_lds4(wave == 0 ? lrs : drs, qd + 2 * C::TILEB + wave * STATB, voff, 0);
+                ld.load(qrs, qd, wave, j * BQ, N);
+                ld.load(ors, qd + QTB, wave, j * BQ, N);
+                // lse2 (waves 0, 1) and D (waves 2, 3) of rows j*BQ + 64*(wave%2) + lane;
+                // rows past the end re-read N-1
+                const int r = 64 * (wave % 2) + lane;
+                buffer_load_lds4(wave < 2 ? lrs : drs, qd + 2 * QTB + (wave / 2) * STATB + 64 * 4 * (wave % 2),
+                                 min(j * BQ + r, N - 1) * 4, 0);
+            };
+
+            // One 32-query block with masks or a causal skip (diagonal and
+            // ragged tiles): S/dP, then P/dS, then dV/dK, in sequence.
+            auto masked_block = [&](const char *Qb, const char *Ob, const float *Lb, const float *Db,
+                                    int qf0) __attribute__((always_inline)) {
+                if (CAUSAL && qf0 + 31 < kw0) return;  // every query before every key
+                f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+                for (int st = 0; st < C::QK_STEPS; ++st) {
+                    s = M::mma(*(const frag *)(Qb + q_rd[st]), kf[st], s);
+                    dp = M::mma(*(const frag *)(Ob + q_rd[st]), vf[st], dp);
+                }
+                f32x4 l4[4], d4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    l4[i] = *(const f32x4 *)(Lb + 8 * i + 4 * h);
+                    d4[i] = *(const f32x4 *)(Db + 8 * i + 4 * h);
+                }
+                const int lo = CAUSAL ? key - qf0 - 4 * h : INT_MIN;  // visible iff acc_row(r,0) >= lo
+                const int hi = N - qf0 - 4 * h;                       // ... and acc_row(r,0) < hi
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[r / 4][r % 4]));
+                    const int ar = acc_row(r, 0);
+                    if (ar < lo || ar >= hi) p = 0.f;
+                    s[r] = p;
+                    dp[r] = p * (dp[r] - d4[r / 4][r % 4]);
+                }
+#pragma unroll
+                for (int st = 0; st < C::PV_STEPS; ++st) {
+                    float pv[KW], sv[KW];
+#pragma unroll
+                    for (int e = 0; e < KW; ++e) {
+                        pv[e] = s[st * KW + e];
+                        sv[e] = dp[st * KW + e];
+                    }
+                    const frag pb = M::pack(pv);
+                    const frag sb = M::pack(sv);
+                    const char *oblk = Ob + 16 * st * C::ROWB;
+                    const char *qblk = Qb + 16 * st * C::ROWB;
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) {
+                        dv[db] = M::mma(tr_read<frag>(oblk, tr[0][db], tr[1][db]), pb, dv[db]);
+                        dk[db] = M::mma(tr_read<frag>(qblk, tr[0][db], tr[1][db]), sb, dk[db]);
+                    }
                 }
             };
 
-            auto tile = [&](int j, auto stage_c) __attribute__((always_inline)) {
+            // A tile every query of which sees every key of this wave: the
+            // schedule above, every LDS operand read two pairs ahead of its
+            // use (a ring of three register slots), fenced so that the
+            // compiler keeps the order.
+            auto full_tile = [&](const char *Qs, const char *Os, const float *Ls, const float *Ds)
+                __attribute__((always_inline)) {
+                f32x16 sa[NBQ], da[NBQ];                        // S then P; dP then dS
+                frag pp[NBQ][C::PV_STEPS], sp[NBQ][C::PV_STEPS];  // P, dS packed for the matrix core
+                frag opr[3][2];
+                f32x4 sl[4], sd[4];                             // lse2, D of 4-row groups
+                auto rd_op = [&](auto gc) __attribute__((always_inline)) {
+                    constexpr int G = decltype(gc)::value;
+                    if constexpr (G < S::NOPS) {
+                        constexpr int kd = S::kind(G), blk = S::block(G), pr = S::pair(G), slot = G % 3;
+                        const char *Qb = Qs + blk * 32 * C::ROWB, *Ob = Os + blk * 32 * C::ROWB;
+                        if constexpr (kd == 0) {
+                            opr[slot][0] = *(const frag *)(Qb + q_rd[pr]);
+                            opr[slot][1] = *(const frag *)(Ob + q_rd[pr]);
+                        } else {
+                            constexpr int st = pr / C::DB, db = pr % C::DB;
+                            opr[slot][0] = tr_read<frag>(Ob + 16 * st * C::ROWB, tr[0][db], tr[1][db]);
+                            opr[slot][1] = tr_read<frag>(Qb + 16 * st * C::ROWB, tr[0][db], tr[1][db]);
+                        }
+                    }
+                };
+                auto mma_op = [&](auto gc) __attribute__((always_inline)) {
+                    constexpr int G = decltype(gc)::value;
+                    constexpr int kd = S::kind(G), blk = S::block(G), pr = S::pair(G), slot = G % 3;
+                    if constexpr (kd == 0) {
+                        sa[blk] = M::mma(opr[slot][0], kf[pr], pr == 0 ? f32x16{} : sa[blk]);
+                        da[blk] = M::mma(opr[slot][1], vf[pr], pr == 0 ? f32x16{} : da[blk]);
+                    } else {
+                        constexpr int st = pr / C::DB, db = pr % C::DB;
+                        dv[db] = M::mma(opr[slot][0], pp[blk][st], dv[db]);
+                        dk[db] = M::mma(opr[slot][1], sp[blk][st], dk[db]);
+                    }
+                };
+                auto extras = [&](auto gc) __attribute__((always_inline)) {
+                    constexpr int G = decltype(gc)::value;
+                    static_for<NBQ>([&](auto bc) __attribute__((always_inline)) {
+                        constexpr int B_ = decltype(bc)::value;
+                        static_for<4>([&](auto rc) __attribute__((always_inline)) {
+                            constexpr int R = decltype(rc)::value;
+                            if constexpr (S::stats_op(B_, R) == G) {
+                                sl[R] = *(const f32x4 *)(Ls + B_ * 32 + 8 * R + 4 * h);
+                                sd[R] = *(const f32x4 *)(Ds + B_ * 32 + 8 * R + 4 * h);
+                            }
+                        });
+                    });
+                };
+                auto elems = [&](auto gc) __attribute__((always_inline)) {
+                    constexpr int G = decltype(gc)::value;
+                    static_for<NBQ>([&](auto bc) __attribute__((always_inline)) {
+                        constexpr int B_ = decltype(bc)::value;
+                        static_for<16>([&](auto ec) __attribute__((always_inline)) {
+                            constexpr int E = decltype(ec)::value;
+                            if constexpr (S::elem_op(B_, E) == G) {
+                                const float p = exp2_hw(__builtin_fmaf(sa[B_][E], c, -sl[E / 4][E % 4]));
+                                sa[B_][E] = p;
+                                da[B_][E] = p * (da[B_][E] - sd[E / 4][E % 4]);
+                                if constexpr (E % KW == KW - 1) {
+                                    pp[B_][E / KW] = pack_regs<T>(sa[B_], E / KW);
+                                    sp[B_][E / KW] = pack_regs<T>(da[B_], E / KW);
+                                }
+                            }
+                        });
+                    });
+                };
+                rd_op(std::integral_constant<int, 0>{});
+                rd_op(std::integral_constant<int, 1>{});
+                static_for<S::NOPS>([&](auto gc) __attribute__((always_inline)) {
+                    constexpr int G = decltype(gc)::value;
+                    rd_op(std::integral_constant<int, G + 2>{});
+                    extras(gc);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_op(gc);
+                    elems(gc);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+
+            // The tiles that need masks are uniform over the workgroup: the
+            // causal diagonal tile first (queries [128 kt, 128 kt + 128) against
+            // keys [128 kt, 128 kt + 128)) and the ragged last tile.  They run
+            // outside the loop of full tiles.
+            auto tile_full = [&](int j, auto stage_c) __attribute__((always_inline)) {
                 constexpr int STAGE = decltype(stage_c)::value;
                 if (j + 1 < nqt) load_tile(j + 1, STAGE ^ 1);
                 const char *Qs = smem + STAGE * STAGEB;
-                const char *Os = Qs + C::TILEB;
-                const float *Ls = (const float *)(Qs + 2 * C::TILEB);
-                const float *Ds = Ls + C::BT;
-#pragma unroll
-                for (int qb = 0; qb < C::NB; ++qb) {
-                    const int qf0 = j * C::BT + qb * 32;  // first query of the block
-                    if (CAUSAL && qf0 + 31 < kw0) continue;  // every query before every key
-                    const bool need_mask = (CAUSAL && qf0 < kw0 + 31) || (qf0 + 32 > N);
-                    const char *Qb = Qs + qb * 32 * C::ROWB;
-                    const char *Ob = Os + qb * 32 * C::ROWB;
-
-                    // S = Q K^T and dP = dO V^T: lane (col, h), register r
-                    // holds query qf0 + acc_row(r, h), key kw0 + col.
-                    f32x16 s = f32x16{}, dp = f32x16{};
-                    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-                    for (int st = 0; st < C::QK_STEPS; ++st) {
-                        s = M::mma(*(const frag *)(Qb + q_rd[st]), kf[st], s);
-                        dp = M::mma(*(const frag *)(Ob + q_rd[st]), vf[st], dp);
-                    }
-                    __builtin_amdgcn_s_setprio(0);
-
-                    // P = 2^(s*c - lse2), dS = P (dP - D); masked pairs (a key
-                    // after the query, or a query row past the end) get 0.
-                    f32x4 l4[4], d4[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        l4[i] = *(const f32x4 *)(Ls + qb * 32 + 8 * i + 4 * h);
-                        d4[i] = *(const f32x4 *)(Ds + qb * 32 + 8 * i + 4 * h);
-                    }
-                    const int lo = CAUSAL ? key - qf0 - 4 * h : INT_MIN;  // visible iff acc_row(r,0) >= lo
-                    const int hi = N - qf0 - 4 * h;                       // ... and acc_row(r,0) < hi
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[r / 4][r % 4]));
-                        if (need_mask) {
-                            const int ar = acc_row(r, 0);
-                            if (ar < lo || ar >= hi) p = 0.f;
-                        }
-                        s[r] = p;
-                        dp[r] = p * (dp[r] - d4[r / 4][r % 4]);
-                    }
-
-                    // dV^T += dO^T P and dK^T += Q^T dS.  Step st contracts
-                    // registers [st*KW, st*KW + KW) of both lane halves: slot
-                    // h*KW + e is query qf0 + acc_row(st*KW + e, h), the order
-                    // the transpose read delivers.
-                    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-                    for (int st = 0; st < C::PV_STEPS; ++st) {
-                        float pv[KW], sv[KW];
-#pragma unroll
-                        for (int e = 0; e < KW; ++e) {
-                            pv[e] = s[st * KW + e];
-                            sv[e] = dp[st * KW + e];
-                        }
-                        const frag pb = M::pack(pv);
-                        const frag sb = M::pack(sv);
-                        const char *oblk = Ob + 16 * st * C::ROWB;
-                        const char *qblk = Qb + 16 * st * C::ROWB;
-#pragma unroll
-                        for (int db = 0; db < C::DB; ++db) {
-                            dv[db] = M::mma(tr_read<frag>(oblk, tr[0][db], tr[1][db]), pb, dv[db]);
-                            dk[db] = M::mma(tr_read<frag>(qblk, tr[0][db], tr[1][db]), sb, dk[db]);
-                        }
-                    }
-                    __builtin_amdgcn_s_setprio(0);
-                }
+                const char *Os = Qs + QTB;
+                const float *Ls = (const float *)(Qs + 2 * QTB);
+                full_tile(Qs, Os, Ls, Ls + BQ);
                 // this wave's loads of the next tile have landed, and after the
                 // barrier every wave's have, and nobody reads the current buffer
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+            };
+            auto tile_masked = [&](int j, int stage) __attribute__((always_inline)) {
+                if (j + 1 < nqt) load_tile(j + 1, stage ^ 1);
+                const char *Qs = smem + stage * STAGEB;
+                const char *Os = Qs + QTB;
+                const float *Ls = (const float *)(Qs + 2 * QTB);
+                const float *Ds = Ls + BQ;
+                for (int qb = 0; qb < NBQ; ++qb)
+                    masked_block(Qs + qb * 32 * C::ROWB, Os + qb * 32 * C::ROWB, Ls + qb * 32,
+                                 Ds + qb * 32, j * BQ + qb * 32);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
             };
@@ -348,12 +514,28 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
             load_tile(qt0, 0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            int j = qt0;
-            for (; j + 1 < nqt; j += 2) {
-                tile(j, std::integral_constant<int, 0>{});
-                tile(j + 1, std::integral_constant<int, 1>{});
+            int j = qt0, stage = 0;
+            if (CAUSAL) {
+                tile_masked(j, 0);
+                ++j;
+                stage = 1;
             }
-            if (j < nqt) tile(j, std::integral_constant<int, 0>{});
+            const int jfull = (N % BQ) ? nqt - 1 : nqt;  // tiles [j, jfull) are full
+            if (stage == 1 && j < jfull) {
+                tile_full(j, std::integral_constant<int, 1>{});
+                ++j;
+                stage = 0;
+            }
+            for (; j + 1 < jfull; j += 2) {
+                tile_full(j, std::integral_constant<int, 0>{});
+                tile_full(j + 1, std::integral_constant<int, 1>{});
+            }
+            if (j < jfull) {
+                tile_full(j, std::integral_constant<int, 0>{});
+                ++j;
+                stage = 1;
+            }
+            if (j < nqt) tile_masked(j, stage);
         }
 
         // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane (col, h) holds key
@@ -379,7 +561,7 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
 // 3. dQ
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                       const T *__restrict__ dO, const float *__restrict__ L2,
                       const float *__restrict__ Dl, float *__restrict__ dQ, int N, int num_qtiles,
@@ -409,7 +591,7 @@ void fa_bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T 
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)(K + kv_head), 0, head_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(V + kv_head), 0, head_bytes, kBufferFlags);
 
-    TileLoader<C> ld;
+    TileLoader<C, C::BT> ld;
     ld.init(wave, lane);
     int k_rd[C::QK_STEPS];
 #pragma unroll
