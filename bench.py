@@ -257,10 +257,12 @@ def main():
                  + int(((gctx + BS - 1) // BS).sum()) * 4 + S * 4)
     gqa_gbs = gqa_bytes / (gqa_avg * 1e-3) / 1e9
 
-    fwd_hash = source_hash("fa_fwd.hip", "fa_device.h")
+    fwd_hash = source_hash("fa_fwd.hip", "fa_device.h", "fa_tile.h")
+    bwd_hash = source_hash("fa_bwd.hip", "fa_device.h", "fa_tile.h")
     dec_hash = source_hash("fa_decode.hip", "fa_device.h")
     fwd_traffic = measured_traffic("fa_fwd_kernel", fwd_hash)
     dec_traffic = measured_traffic("fa_decode_partition_kernel", dec_hash)
+    bwd_traffic = measured_traffic("fa_bwd", bwd_hash)
 
     result = {
         "metric": "attn fwd TFLOP/s + % bf16 MFMA peak (N=8192,d=128,causal); decode HBM GB/s",
@@ -317,6 +319,7 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2),
                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                             "traffic": bwd_traffic,
                              "kernel": "fa_bwd_prep_kernel + fa_bwd_dkdv_kernel + fa_bwd_dq_kernel "
                                        "(bf16, d=128, causal)",
                              "algorithmic_per_launch": bwd_flops}},
