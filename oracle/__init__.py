@@ -17,6 +17,7 @@ Functions (each cites the page passages it follows in ``oracle.c``):
                                                       both loop orders
   attention_bwd(q, k, v, dout, scale, causal, rows=None, keys=None)
                                                       gradients dQ, dK, dV
+  e4m3_encode / e4m3_decode, quant_fp8, dequant_fp8  block-scaled FP8 (E4M3)
   paged_decode(...), paged_decode_partitioned(...)    single-query decode
   widen(x)                                            exact fp64 view
 """
@@ -70,6 +71,14 @@ def _load():
                                                     vp, vp, vp, vp, vp, i]
     lib.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, d, i, vp, i64, vp, i64,
                                          vp, vp, vp, vp, i]
+    lib.oracle_e4m3_encode.argtypes = [vp, i64, vp]
+    lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
+    lib.oracle_fp8_codes_len.argtypes = [i, i, i, i, i]
+    lib.oracle_fp8_codes_len.restype = i64
+    lib.oracle_quant_fp8.argtypes = [vp, i, i, i, i, i, i, vp, vp]
+    lib.oracle_dequant_fp8.argtypes = [vp, vp, i, i, i, i, i, vp]
+    for name in ("oracle_e4m3_encode", "oracle_e4m3_decode", "oracle_quant_fp8", "oracle_dequant_fp8"):
+        getattr(lib, name).restype = i
     for name in ("oracle_widen", "oracle_attention", "oracle_probs", "oracle_tiled_fa1",
                  "oracle_tiled_fa2", "oracle_paged_decode", "oracle_paged_decode_partitioned",
                  "oracle_attention_bwd"):
@@ -190,6 +199,55 @@ def attention_bwd(q, k, v, dout, scale, causal, rows=None, keys=None, nthreads=N
         nthreads or default_threads())
     _check(st, "oracle_attention_bwd")
     return dict(dq=dq, dk=dk, dv=dv, D=D)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """E4M3 (OCP E4M3FN) codes of fp64 values, round to nearest even, saturating at 448."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(a.shape, dtype=np.uint8)
+    _check(_load().oracle_e4m3_encode(_p(a), a.size, _p(out)), "oracle_e4m3_encode")
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """fp64 values of E4M3 codes (NaN for S.1111.111)."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, dtype=np.float64)
+    _check(_load().oracle_e4m3_decode(_p(c), c.size, _p(out)), "oracle_e4m3_decode")
+    return out
+
+
+def fp8_codes_shape(layout, B, H, N, d):
+    """Shape of the code tensor: [B, H, N, d] (layout 0) or [B, H, ceil(N/64), d, 64] (layout 1)."""
+    return (B, H, N, d) if layout == 0 else (B, H, (N + 63) // 64, d, 64)
+
+
+def quant_fp8(x, layout):
+    """Block-scaled E4M3 quantisation of x [B, H, N, d] (128-row blocks, power-of-two scales).
+
+    Returns (codes uint8 of fp8_codes_shape(layout, ...), exps int32 [B, H, ceil(N/128)]).
+    """
+    t, code = _host(x)
+    if t.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
+    B, H, N, d = t.shape
+    codes = np.empty(fp8_codes_shape(layout, B, H, N, d), dtype=np.uint8)
+    exps = np.empty((B, H, (N + 127) // 128), dtype=np.int32)
+    _check(_load().oracle_quant_fp8(_p(t), code, B, H, N, d, int(layout), _p(codes), _p(exps)),
+           "oracle_quant_fp8")
+    return codes, exps
+
+
+def dequant_fp8(codes, exps, B, H, N, d, layout) -> np.ndarray:
+    """fp64 values [B, H, N, d] of block-scaled E4M3 codes (value(code) * 2^e)."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    e = np.ascontiguousarray(np.asarray(exps, dtype=np.int32))
+    if c.shape != fp8_codes_shape(layout, B, H, N, d) or e.shape != (B, H, (N + 127) // 128):
+        raise ValueError("codes / exps shape mismatch")
+    out = np.empty((B, H, N, d), dtype=np.float64)
+    _check(_load().oracle_dequant_fp8(_p(c), _p(e), B, H, N, d, int(layout), _p(out)),
+           "oracle_dequant_fp8")
+    return out
 
 
 def probs(q, k, scale, causal):

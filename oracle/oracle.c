@@ -849,3 +849,135 @@ out:
     free(need); free(m); free(l); free(D);
     return rc;
 }
+
+/* ------------------------------------------------------------------ */
+/* Block-scaled FP8 (E4M3) quantisation                                 */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [YJ] 9.2 item 3: FP8 attention keeps a separate scale factor for each
+ * block of the inputs so that each block uses the FP8 range.  Readings fixed
+ * here (the pages name the technique only):
+ *   - the FP8 format is E4M3 as defined by the OCP 8-bit floating point
+ *     specification ("E4M3FN"): 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+ *     subnormals, no infinities, S.1111.111 = NaN, largest finite 448;
+ *   - a block is 128 consecutive rows of one (b, h) with all d columns;
+ *   - the block's scale is the power of two 2^e with e = floor(log2 amax) - 7
+ *     (amax = largest magnitude in the block; e = 0 for an all-zero block),
+ *     so that every scaled value is below 256 and the scaling is exact;
+ *   - code = E4M3 rounding (to nearest, ties to even) of x * 2^-e;
+ *     dequantised value = value(code) * 2^e.
+ */
+
+/* E4M3 code of a finite double, round to nearest even, saturating at 448 */
+static uint8_t or_e4m3_encode_one(double x)
+{
+    uint8_t s = (x < 0 || (x == 0 && signbit(x))) ? 0x80 : 0;
+    double a = fabs(x);
+    if (isnan(x)) return (uint8_t)(s | 0x7f);
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal: a multiple of 2^-9 with a 3-bit mantissa */
+        double m = nearbyint(ldexp(a, 9)); /* 0 .. 8; 8 is the smallest normal */
+        return (uint8_t)(s | (uint8_t)m);
+    }
+    int ex;
+    frexp(a, &ex); /* a = f 2^ex, f in [0.5, 1) */
+    int E = ex - 1;  /* a in [2^E, 2^(E+1)) */
+    double m = nearbyint((ldexp(a, -E) - 1.0) * 8.0); /* 0 .. 8 */
+    if (m == 8.0) { m = 0.0; E += 1; }
+    if (E > 8 || (E == 8 && m > 6.0)) return (uint8_t)(s | 0x7e); /* saturate to 448 */
+    return (uint8_t)(s | (uint8_t)((E + 7) << 3) | (uint8_t)m);
+}
+
+static double or_e4m3_decode_one(uint8_t c)
+{
+    int s = c >> 7, ef = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (ef == 15 && m == 7) return NAN;
+    if (ef == 0) v = ldexp((double)m, -9);
+    else v = ldexp(1.0 + m / 8.0, ef - 7);
+    return s ? -v : v;
+}
+
+int oracle_e4m3_encode(const double *x, int64_t n, uint8_t *codes)
+{
+    if ((!x || !codes) && n > 0) return -1;
+    for (int64_t i = 0; i < n; ++i) codes[i] = or_e4m3_encode_one(x[i]);
+    return 0;
+}
+
+int oracle_e4m3_decode(const uint8_t *codes, int64_t n, double *x)
+{
+    if ((!x || !codes) && n > 0) return -1;
+    for (int64_t i = 0; i < n; ++i) x[i] = or_e4m3_decode_one(codes[i]);
+    return 0;
+}
+
+/*
+ * Code layouts:
+ *   layout 0 (Q, K): codes [B, H, N, d], row-major like the input;
+ *   layout 1 (V):    codes [B, H, T, d, 64] with T = ceil(N / 64): each tile
+ *                    of 64 keys is stored d-major (element (key, c) of tile t
+ *                    at [t][c][key - 64 t]); keys >= N hold code 0.
+ * exps: [B, H, ceil(N / 128)] int32, the block exponents e.
+ */
+static int64_t or_fp8_code_index(int layout, int64_t bh, int64_t N, int d, int64_t i, int c)
+{
+    if (layout == 0) return (bh * N + i) * d + c;
+    int64_t T = (N + 63) / 64;
+    return ((bh * T + i / 64) * d + c) * 64 + (i % 64);
+}
+
+int64_t oracle_fp8_codes_len(int layout, int B, int H, int N, int d)
+{
+    if (layout == 0) return (int64_t)B * H * N * d;
+    return (int64_t)B * H * ((N + 63) / 64) * d * 64;
+}
+
+int oracle_quant_fp8(const void *x, int dtype, int B, int H, int N, int d, int layout,
+                     uint8_t *codes, int32_t *exps)
+{
+    if (!x || !codes || !exps || B < 1 || H < 1 || N < 1 || d < 1) return -1;
+    if (or_elem_bytes(dtype) == 0 || (layout != 0 && layout != 1)) return -1;
+    int64_t nblk = (N + 127) / 128;
+    memset(codes, 0, (size_t)oracle_fp8_codes_len(layout, B, H, N, d));
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        for (int64_t blk = 0; blk < nblk; ++blk) {
+            int64_t r0 = blk * 128, r1 = r0 + 128 < N ? r0 + 128 : N;
+            double amax = 0.0;
+            for (int64_t i = r0; i < r1; ++i)
+                for (int c = 0; c < d; ++c) {
+                    double a = fabs(or_load(x, dtype, (bh * N + i) * d + c));
+                    if (a > amax) amax = a;
+                }
+            int e = 0;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);
+                e = (ex - 1) - 7;
+            }
+            exps[bh * nblk + blk] = e;
+            for (int64_t i = r0; i < r1; ++i)
+                for (int c = 0; c < d; ++c)
+                    codes[or_fp8_code_index(layout, bh, N, d, i, c)] =
+                        or_e4m3_encode_one(ldexp(or_load(x, dtype, (bh * N + i) * d + c), -e));
+        }
+    }
+    return 0;
+}
+
+/* dequantised values in the natural layout: out [B, H, N, d] fp64 */
+int oracle_dequant_fp8(const uint8_t *codes, const int32_t *exps, int B, int H, int N, int d,
+                       int layout, double *out)
+{
+    if (!codes || !exps || !out || B < 1 || H < 1 || N < 1 || d < 1) return -1;
+    if (layout != 0 && layout != 1) return -1;
+    int64_t nblk = (N + 127) / 128;
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
+        for (int64_t i = 0; i < N; ++i)
+            for (int c = 0; c < d; ++c)
+                out[(bh * N + i) * d + c] =
+                    ldexp(or_e4m3_decode_one(codes[or_fp8_code_index(layout, bh, N, d, i, c)]),
+                          exps[bh * nblk + i / 128]);
+    return 0;
+}

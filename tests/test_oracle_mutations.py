@@ -17,7 +17,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_decode.py",
-              "tests/test_oracle_tiling.py", "tests/test_oracle_bwd.py"]
+              "tests/test_oracle_tiling.py", "tests/test_oracle_bwd.py", "tests/test_oracle_fp8.py"]
 
 # (name, text in oracle.c, replacement); the text must occur in the source
 MUTATIONS = [
@@ -93,6 +93,24 @@ MUTATIONS = [
     ("bwd_causal_skips_diagonal",
      "for (int64_t i = x->causal ? j : 0; i < N; ++i) {",
      "for (int64_t i = x->causal ? j + 1 : 0; i < N; ++i) {"),
+    ("e4m3_exponent_bias_8",
+     "return (uint8_t)(s | (uint8_t)((E + 7) << 3) | (uint8_t)m);",
+     "return (uint8_t)(s | (uint8_t)((E + 8) << 3) | (uint8_t)m);"),
+    ("e4m3_subnormal_step",
+     "double m = nearbyint(ldexp(a, 9));",
+     "double m = nearbyint(ldexp(a, 10));"),
+    ("e4m3_mantissa_truncated",
+     "double m = nearbyint((ldexp(a, -E) - 1.0) * 8.0);",
+     "double m = floor((ldexp(a, -E) - 1.0) * 8.0);"),
+    ("e4m3_decode_bias",
+     "else v = ldexp(1.0 + m / 8.0, ef - 7);",
+     "else v = ldexp(1.0 + m / 8.0, ef - 8);"),
+    ("fp8_block_exponent_offset",
+     "e = (ex - 1) - 7;",
+     "e = (ex - 1) - 8;"),
+    ("fp8_tile_layout_swapped",
+     "return ((bh * T + i / 64) * d + c) * 64 + (i % 64);",
+     "return ((bh * T + i / 64) * 64 + (i % 64)) * d + c;"),
     ("bwd_group_mapping",
      "for (int64_t h = g * group; h < (g + 1) * group; ++h) {",
      "for (int64_t h = g; h < x->H; h += x->Hkv) {"),
