@@ -11,7 +11,9 @@ One step = one pass of the whole path over one batch of synthetic input:
      heads (4 query heads per kv head);
   4. fa_fwd_gqa on the forward workload with 8 kv heads (fwd_gqa);
   5. fa_bwd on the forward workload (bwd): dQ, dK, dV for a seeded N(0,1)
-     upstream gradient, from step 1's o and lse.
+     upstream gradient, from step 1's o and lse;
+  6. fa_fwd_fp8 on the forward workload quantised to block-scaled E4M3
+     (fwd_fp8), and fa_quant_fp8 of its q, k, v (quant_fp8).
 Inputs are generated on the host with fixed seeds and copied to HBM before
 the timed region.  The timed region runs K steps between two device
 synchronisations; each kernel call is bracketed by HIP events recorded on the
@@ -37,6 +39,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak (published)
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (published)
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
@@ -186,6 +189,13 @@ def main():
     bdv = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     bws = torch.empty(fa.fa_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
 
+    log("quantising the forward inputs to block-scaled E4M3")
+    q8, qe8 = fa.quant_fp8(qd, 0)
+    k8, ke8 = fa.quant_fp8(kd, 0)
+    v8, ve8 = fa.quant_fp8(vd, 1)
+    o8 = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    lse8 = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
     stream = torch.cuda.current_stream()
 
     def step(evs=None):
@@ -209,13 +219,21 @@ def main():
                   stream=stream)
         if evs:
             evs[5].record(stream)
+        fa.fa_fwd_fp8(q8, k8, v8, qe8, ke8, ve8, o8, lse8, B, H, H, N, d, fscale, True, stream=stream)
+        if evs:
+            evs[6].record(stream)
+        fa.fa_quant_fp8(qd, B, H, N, d, 0, q8, qe8, stream=stream)
+        fa.fa_quant_fp8(kd, B, H, N, d, 0, k8, ke8, stream=stream)
+        fa.fa_quant_fp8(vd, B, H, N, d, 1, v8, ve8, stream=stream)
+        if evs:
+            evs[7].record(stream)
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -237,11 +255,20 @@ def main():
     # dK, dQ), 2.5 times the forward's two
     bwd_flops = 2.5 * fcfg.flops()
     bwd_tflops = bwd_flops / (bwd_avg * 1e-3) / 1e12
+    f8_ms = [e[5].elapsed_time(e[6]) for e in evs]
+    f8_avg = sum(f8_ms) / len(f8_ms)
+    f8_tflops = fcfg.flops() / (f8_avg * 1e-3) / 1e12
+    qz_ms = [e[6].elapsed_time(e[7]) for e in evs]
+    qz_avg = sum(qz_ms) / len(qz_ms)
+    nel = B * H * N * d
+    qz_bytes = 3 * nel * qd.element_size() + 2 * nel + fa.fa_fp8_codes_bytes(B, H, N, d, 1) \
+        + 3 * B * H * ((N + 127) // 128) * 4
+    qz_gbs = qz_bytes / (qz_avg * 1e-3) / 1e9
 
     # quick sanity of the last step's results (full parity lives in the tests)
     finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item()
                   and torch.isfinite(gout).all().item() and torch.isfinite(go).all().item()
-                  and all(torch.isfinite(t).all().item() for t in (bdq, bdk, bdv)))
+                  and all(torch.isfinite(t).all().item() for t in (bdq, bdk, bdv, o8)))
 
     flops = fcfg.flops()
     tflops = flops / (fwd_avg * 1e-3) / 1e12
@@ -323,6 +350,22 @@ def main():
                              "kernel": "fa_bwd_prep_kernel + fa_bwd_dkdv_kernel + fa_bwd_dq_kernel "
                                        "(bf16, d=128, causal)",
                              "algorithmic_per_launch": bwd_flops}},
+        "fwd_fp8": {"metric": "attention forward TFLOP/s on block-scaled E4M3 inputs",
+                    "value": round(f8_tflops, 2), "unit": "TFLOP/s", "workload": fcfg.name + ", E4M3",
+                    "kernel_ms_avg": round(f8_avg, 4), "kernel_ms_min": round(min(f8_ms), 4),
+                    "speedup_vs_bf16": round(fwd_avg / f8_avg, 3),
+                    "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 2),
+                                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4),
+                                 "kernel": "fa_fwd_fp8_kernel<causal>",
+                                 "algorithmic_per_launch": fcfg.flops()}},
+        "quant_fp8": {"metric": "block-scaled E4M3 quantisation of q, k, v (HBM GB/s)",
+                      "value": round(qz_gbs, 1), "unit": "GB/s", "ms_avg": round(qz_avg, 4),
+                      "roofline": {"bound": "hbm", "achieved": round(qz_gbs, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(qz_gbs / PEAK_HBM_GBS, 4),
+                                   "kernel": "fa_quant_fp8_kernel x3",
+                                   "algorithmic_per_launch": qz_bytes}},
         "decode_gqa": {"metric": "paged decode HBM bandwidth, 4 query heads per kv head",
                        "value": round(gqa_gbs, 1), "unit": "GB/s",
                        "workload": gcfg.name, "sum_ctx": int(gctx.sum()),

@@ -20,13 +20,15 @@ import torch
 
 __all__ = [
     "FA_F32", "FA_BF16", "FA_F16", "FA_DECODE_PARTITION_TOKENS", "FAError", "fa_fwd_gqa",
-    "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
-    "fa_paged_decode_workspace_size", "fa_strerror", "forward", "backward", "paged_decode",
-    "lib_path", "load_library",
+    "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_quant_fp8",
+    "fa_fwd_fp8", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror", "forward",
+    "backward", "quant_fp8", "forward_fp8", "paged_decode", "lib_path", "load_library",
+    "FA_FP8_BLOCK_ROWS",
 ]
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_DECODE_PARTITION_TOKENS = 256  # must match include/fa.h
+FA_FP8_BLOCK_ROWS = 128           # must match include/fa.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -66,6 +68,12 @@ def load_library():
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_fp8_codes_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_fp8_codes_bytes.restype = sz
+    lib.fa_quant_fp8.argtypes = [vp, i, i, i, i, i, i, vp, vp, vp]
+    lib.fa_quant_fp8.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_paged_decode_workspace_size.argtypes = [i, i, i, i]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
@@ -157,6 +165,31 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, wo
         raise FAError(st, "fa_bwd")
 
 
+def fa_fp8_codes_bytes(B, H, N, d, layout) -> int:
+    """C entry point ``fa_fp8_codes_bytes`` (bytes; 0 if invalid)."""
+    return int(load_library().fa_fp8_codes_bytes(int(B), int(H), int(N), int(d), int(layout)))
+
+
+def fa_quant_fp8(x, B, H, N, d, layout, codes, exps, dtype=None, stream=None):
+    """C entry point ``fa_quant_fp8``: block-scaled E4M3 codes and exponents of x."""
+    if dtype is None:
+        dtype = _dtype_code(x.dtype)
+    st = load_library().fa_quant_fp8(_ptr(x), int(dtype), int(B), int(H), int(N), int(d),
+                                     int(layout), _ptr(codes), _ptr(exps), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_quant_fp8")
+
+
+def fa_fwd_fp8(q8, k8, v8, q_exp, k_exp, v_exp, o, lse, B, H, Hkv, N, d, scale, causal,
+               stream=None):
+    """C entry point ``fa_fwd_fp8``: the forward pass on block-scaled E4M3 inputs."""
+    st = load_library().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_exp), _ptr(k_exp),
+                                   _ptr(v_exp), _ptr(o), _ptr(lse), int(B), int(H), int(Hkv),
+                                   int(N), int(d), float(scale), int(bool(causal)), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_fwd_fp8")
+
+
 def fa_paged_decode_workspace_size(num_seqs, num_heads, head_size, max_context_len) -> int:
     """C entry point ``fa_paged_decode_workspace_size`` (bytes; 0 if invalid)."""
     return int(load_library().fa_paged_decode_workspace_size(
@@ -241,6 +274,37 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, st
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace,
            stream=stream)
     return dq, dk, dv
+
+
+def quant_fp8(x, layout, stream=None):
+    """Allocate and fill the E4M3 codes (uint8, flat) and block exponents (int32
+    [B, H, ceil(N/128)]) of x [B, H, N, d]; layout 0 for q and k, 1 for v."""
+    _check_dev("x", x)
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
+    B, H, N, d = x.shape
+    codes = torch.empty(max(fa_fp8_codes_bytes(B, H, N, d, layout), 16), dtype=torch.uint8,
+                        device=x.device)
+    exps = torch.empty((B, H, (N + FA_FP8_BLOCK_ROWS - 1) // FA_FP8_BLOCK_ROWS),
+                       dtype=torch.int32, device=x.device)
+    fa_quant_fp8(x, B, H, N, d, layout, codes, exps, stream=stream)
+    return codes, exps
+
+
+def forward_fp8(q8, k8, v8, q_exp, k_exp, v_exp, B, H, Hkv, N, d=128, scale=None, causal=False,
+                stream=None):
+    """Allocate o (fp32) and lse (fp32) and run ``fa_fwd_fp8``; returns (o, lse)."""
+    for n, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _check_dev(n, t, torch.uint8)
+    for n, t in (("q_exp", q_exp), ("k_exp", k_exp), ("v_exp", v_exp)):
+        _check_dev(n, t, torch.int32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, v8, q_exp, k_exp, v_exp, o, lse, B, H, Hkv, N, d, scale, causal,
+               stream=stream)
+    return o, lse
 
 
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,

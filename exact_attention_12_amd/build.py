@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_capi.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_decode.hip", "fa_capi.cpp")]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU
 # instructions; hipcc's host pass warns that it does not know the feature.

@@ -24,6 +24,11 @@ hipError_t bwd_dispatch(const void *q, const void *k, const void *v, const float
                         int H, int Hkv, int N, int d, float scale, int causal, int dtype,
                         void *workspace, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int H, int N);
+hipError_t quant_fp8_dispatch(const void *x, int dtype, int B, int H, int N, int d, int layout,
+                              void *codes, int32_t *exps, hipStream_t stream);
+hipError_t fwd_fp8_dispatch(const void *q8, const void *k8, const void *v8, const int32_t *qe,
+                            const int32_t *ke, const int32_t *ve, float *o, float *lse, int B, int H,
+                            int Hkv, int N, float scale, int causal, hipStream_t stream);
 }  // namespace fa
 
 namespace {
@@ -146,6 +151,67 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const float *
     }
     const hipError_t e = fa::bwd_dispatch(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale,
                                           causal ? 1 : 0, dtype, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" size_t fa_fp8_codes_bytes(int B, int H, int N, int d, int layout)
+{
+    if (B < 1 || H < 1 || N < 1 || d < 1 || (layout != 0 && layout != 1)) return 0;
+    const size_t rows = layout == 0 ? (size_t)N : (size_t)(N + 63) / 64 * 64;
+    return (size_t)B * H * rows * d;
+}
+
+extern "C" int fa_quant_fp8(const void *x, int dtype, int B, int H, int N, int d, int layout,
+                            void *codes, int32_t *exps, void *stream)
+{
+    if (!x || !codes || !exps) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || d < 1 || (layout != 0 && layout != 1)) return FA_ERR_INVALID_ARG;
+    const int es = elem_bytes(dtype);
+    if (es == 0) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const int64_t nblk = ((int64_t)N + FA_FP8_BLOCK_ROWS - 1) / FA_FP8_BLOCK_ROWS;
+    if ((int64_t)B * H * nblk > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)N * d * es > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(exps, 4)) return FA_ERR_ALIGNMENT;
+    const uint64_t x_bytes = (uint64_t)B * H * N * d * es;
+    const uint64_t c_bytes = fa_fp8_codes_bytes(B, H, N, d, layout);
+    const uint64_t e_bytes = (uint64_t)B * H * nblk * 4;
+    if (overlap(codes, c_bytes, x, x_bytes) || overlap(exps, e_bytes, x, x_bytes) ||
+        overlap(codes, c_bytes, exps, e_bytes))
+        return FA_ERR_INVALID_ARG;
+    const hipError_t e = fa::quant_fp8_dispatch(x, dtype, B, H, N, d, layout, codes, exps,
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd_fp8(const void *q8, const void *k8, const void *v8, const int32_t *q_exp,
+                          const int32_t *k_exp, const int32_t *v_exp, float *o, float *lse, int B,
+                          int H, int Hkv, int N, int d, float scale, int causal, void *stream)
+{
+    if (!q8 || !k8 || !v8 || !q_exp || !k_exp || !v_exp || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    const int64_t qtiles = ((int64_t)N + kFwdRowsPerWorkgroup - 1) / kFwdRowsPerWorkgroup;
+    if ((int64_t)B * H * qtiles > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)((N + 63) / 64) * 64 * d > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) ||
+        !aligned(q_exp, 4) || !aligned(k_exp, 4) || !aligned(v_exp, 4) || !aligned(lse, 4))
+        return FA_ERR_ALIGNMENT;
+    const int64_t nblk = ((int64_t)N + FA_FP8_BLOCK_ROWS - 1) / FA_FP8_BLOCK_ROWS;
+    const uint64_t rows = (uint64_t)B * H * N;
+    const uint64_t o_bytes = rows * d * 4, l_bytes = rows * 4;
+    const void *ins[6] = {q8, k8, v8, q_exp, k_exp, v_exp};
+    const uint64_t in_bytes[6] = {fa_fp8_codes_bytes(B, H, N, d, 0), fa_fp8_codes_bytes(B, Hkv, N, d, 0),
+                                  fa_fp8_codes_bytes(B, Hkv, N, d, 1), (uint64_t)B * H * nblk * 4,
+                                  (uint64_t)B * Hkv * nblk * 4, (uint64_t)B * Hkv * nblk * 4};
+    if (overlap(o, o_bytes, lse, l_bytes)) return FA_ERR_INVALID_ARG;
+    for (int i = 0; i < 6; ++i)
+        if (overlap(o, o_bytes, ins[i], in_bytes[i]) || overlap(lse, l_bytes, ins[i], in_bytes[i]))
+            return FA_ERR_INVALID_ARG;
+    const hipError_t e = fa::fwd_fp8_dispatch(q8, k8, v8, q_exp, k_exp, v_exp, o, lse, B, H, Hkv, N,
+                                              scale, causal ? 1 : 0, (hipStream_t)stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -16,7 +16,11 @@
  *     upstream gradient dO, with the blocks of P recomputed on chip from Q,
  *     K and the saved lse instead of being stored (youngju.dev section 7.2).
  *
- *  3. fa_paged_decode: single-query attention of one new token per sequence
+ *  3. fa_quant_fp8 / fa_fwd_fp8: the forward pass in FP8 (E4M3) with one
+ *     scale factor per block of the inputs (block quantisation, youngju.dev
+ *     section 9.2 item 3).
+ *
+ *  4. fa_paged_decode: single-query attention of one new token per sequence
  *     against its context stored in a paged (block-table) KV cache, split
  *     into context partitions whose partial results (m, l, O) are merged with
  *     Eq. (4) of "Flash Attention" generalised to P parts.  The cache layout
@@ -149,6 +153,64 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
            const void *dout, float *dq, float *dk, float *dv, int B, int H, int Hkv, int N, int d,
            float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
            void *stream);
+
+/*
+ * Block-scaled FP8 (youngju.dev section 9.2, item 3: FP8 with a separate
+ * scale factor per block).  Format: OCP E4M3 ("E4M3FN": 1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, subnormals, largest finite 448).  A
+ * block is FA_FP8_BLOCK_ROWS consecutive rows of one (b, h) with all d
+ * columns; its scale is 2^e with e = floor(log2 amax) - 7 (amax = largest
+ * magnitude in the block; e = 0 for an all-zero block), and element x is
+ * stored as the E4M3 rounding (nearest, ties to even) of x * 2^-e, its value
+ * being value(code) * 2^e.
+ *
+ * Code layouts:
+ *   layout 0 (q, k): [B, H, N, d] bytes, like the input;
+ *   layout 1 (v):    [B, H, ceil(N/64), d, 64] bytes: each tile of 64 keys is
+ *                    stored d-major (element (key, c) of tile t at
+ *                    [t][c][key - 64 t]); keys >= N hold code 0.
+ * Exponents: [B, H, ceil(N / FA_FP8_BLOCK_ROWS)] int32.
+ */
+#define FA_FP8_BLOCK_ROWS 128
+
+/* fa_fp8_codes_bytes -- bytes of the code tensor of a [B, H, N, d] input in
+ * `layout` (0 or 1); 0 for invalid sizes. */
+size_t fa_fp8_codes_bytes(int B, int H, int N, int d, int layout);
+
+/*
+ * fa_quant_fp8 -- block-scaled E4M3 quantisation of x.
+ *
+ *   x       : [B, H, N, d] contiguous, element type `dtype` (FA_F32, FA_BF16
+ *             or FA_F16), finite, 16-byte aligned.  Read only.
+ *   layout  : 0 or 1 (see above); d: 64 or 128 (else FA_ERR_UNSUPPORTED).
+ *   codes   : fa_fp8_codes_bytes(B, H, N, d, layout) bytes, 16-byte aligned.
+ *             Written.
+ *   exps    : [B, H, ceil(N / FA_FP8_BLOCK_ROWS)] int32, 4-byte aligned.
+ *             Written.
+ * codes and exps must not overlap x or each other.
+ */
+int fa_quant_fp8(const void *x, int dtype, int B, int H, int N, int d, int layout, void *codes,
+                 int32_t *exps, void *stream);
+
+/*
+ * fa_fwd_fp8 -- the attention forward on block-scaled E4M3 inputs.
+ *
+ *   q8, q_exp : q codes in layout 0 ([B, H, N, d]) and exponents [B, H, nblk].
+ *   k8, k_exp : k codes in layout 0 ([B, Hkv, N, d]) and exponents [B, Hkv, nblk].
+ *   v8, v_exp : v codes in layout 1 ([B, Hkv, ceil(N/64), d, 64]) and
+ *               exponents [B, Hkv, nblk].
+ *   o, lse    : as fa_fwd: o [B, H, N, d] fp32 and lse [B, H, N] fp32 of
+ *               attention on the dequantised values (value(code) * 2^e).
+ *   Hkv, B, H, N, scale, causal : as fa_fwd_gqa.  d: 128 (else
+ *               FA_ERR_UNSUPPORTED).
+ * Products of codes are exact and accumulate in fp32; the probabilities
+ * are rounded to E4M3 for the P.V product and normalised by the sum of the
+ * unrounded probabilities.  Code pointers and o 16-byte aligned, exponents
+ * and lse 4-byte aligned; o and lse must not overlap any input.
+ */
+int fa_fwd_fp8(const void *q8, const void *k8, const void *v8, const int32_t *q_exp,
+               const int32_t *k_exp, const int32_t *v_exp, float *o, float *lse, int B, int H,
+               int Hkv, int N, int d, float scale, int causal, void *stream);
 
 /*
  * fa_paged_decode_workspace_size -- bytes of device workspace that

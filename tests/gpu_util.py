@@ -20,6 +20,15 @@ DECODE_TOL = dict(o_max=1e-2, o_mean=1e-3)
 # the mean reference magnitude, each with a small absolute floor for
 # gradients that are exactly zero in the reference (N = 1).
 BWD_TOL = dict(max_rel=2e-2, mean_rel=5e-3, floor=1e-5)
+# Block-scaled FP8 forward, against the oracle on the dequantised inputs.
+# The only rounding beyond fp32 accumulation is that of each probability to
+# E4M3 before the P.V product: |P^ - P~| <= 2^-4 P~ in the normal range and
+# <= 2^-10 below it, and O is normalised by the unrounded sum.  Hence, per
+# element, |dO_ic| <= 2^-4 sum_j w_ij |v_jc| + (subnormal terms), with w the
+# exact softmax weights: the test computes sum_j w_ij |v_jc| with the oracle
+# (attention applied to |V|) and allows 2^-4 of it plus 2^-8.  lse uses the
+# unrounded sum, as in the 16-bit forward.
+FP8_TOL = dict(rel=2.0 ** -4, abs=2.0 ** -8, lse_max=1e-3)
 
 
 _LOG = os.environ.get("FA_PROGRESS_LOG") or os.path.join(

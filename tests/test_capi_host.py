@@ -23,13 +23,14 @@ P = 0x10000  # a 256-byte aligned, non-null fake device address; never dereferen
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function(fa_lib):
     names = declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_gqa", "fa_paged_decode",
-                     "fa_paged_decode_workspace_size", "fa_strerror"]
+    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_fwd", "fa_fwd_fp8",
+                     "fa_fwd_gqa", "fa_paged_decode", "fa_paged_decode_workspace_size",
+                     "fa_quant_fp8", "fa_strerror"]
     for n in names:
         assert hasattr(fa_lib, n), n
 
@@ -45,6 +46,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"FA_DECODE_PARTITION_TOKENS\s+(\d+)", text).group(1)) == \
         fa.FA_DECODE_PARTITION_TOKENS
+    assert int(re.search(r"FA_FP8_BLOCK_ROWS\s+(\d+)", text).group(1)) == fa.FA_FP8_BLOCK_ROWS
     for name, val in [("FA_F32", 0), ("FA_BF16", 1), ("FA_F16", 2)]:
         assert re.search(r"%s\s*=\s*%d" % (name, val), text)
         assert getattr(fa, name) == val
@@ -145,6 +147,50 @@ def test_bwd_workspace_size(fa_lib):
     assert fa.fa_bwd_workspace_size(1, 1, 3) == 256
     assert fa.fa_bwd_workspace_size(0, 1, 3) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 0) == 0
+
+
+def quant(lib, x=P, dtype=1, B=1, H=2, N=100, d=128, layout=0, codes=FAR[0], exps=FAR[1]):
+    return lib.fa_quant_fp8(x, dtype, B, H, N, d, layout, codes, exps, None)
+
+
+def test_quant_fp8_validation(fa_lib):
+    assert quant(fa_lib, x=0) == INVALID
+    assert quant(fa_lib, exps=0) == INVALID
+    assert quant(fa_lib, layout=2) == INVALID
+    assert quant(fa_lib, dtype=9) == INVALID
+    assert quant(fa_lib, N=0) == INVALID
+    assert quant(fa_lib, d=96) == UNSUPPORTED
+    assert quant(fa_lib, codes=FAR[0] + 8) == ALIGN
+    assert quant(fa_lib, exps=FAR[1] + 2) == ALIGN
+    assert quant(fa_lib, codes=P + 64) == INVALID          # codes overlap x
+    assert quant(fa_lib, exps=FAR[0] + 16) == INVALID      # exps overlap codes
+    assert quant(fa_lib, B=1 << 16, H=1 << 16, N=1 << 10) == UNSUPPORTED
+
+
+def test_fp8_codes_bytes(fa_lib):
+    assert fa.fa_fp8_codes_bytes(2, 3, 100, 128, 0) == 2 * 3 * 100 * 128
+    assert fa.fa_fp8_codes_bytes(2, 3, 100, 128, 1) == 2 * 3 * 128 * 128
+    assert fa.fa_fp8_codes_bytes(1, 1, 64, 64, 1) == 64 * 64
+    assert fa.fa_fp8_codes_bytes(1, 1, 0, 64, 0) == 0
+    assert fa.fa_fp8_codes_bytes(1, 1, 8, 64, 3) == 0
+
+
+def fwd8(lib, q8=P, k8=P, v8=P, qe=P, ke=P, ve=P, o=FAR[0], lse=FAR[1], B=1, H=2, Hkv=1, N=100,
+         d=128, scale=0.088, causal=1):
+    return lib.fa_fwd_fp8(q8, k8, v8, qe, ke, ve, o, lse, B, H, Hkv, N, d, scale, causal, None)
+
+
+def test_fwd_fp8_validation(fa_lib):
+    assert fwd8(fa_lib, q8=0) == INVALID
+    assert fwd8(fa_lib, ve=0) == INVALID
+    assert fwd8(fa_lib, Hkv=3) == INVALID
+    assert fwd8(fa_lib, scale=-1.0) == INVALID
+    assert fwd8(fa_lib, d=64) == UNSUPPORTED
+    assert fwd8(fa_lib, v8=P + 8) == ALIGN
+    assert fwd8(fa_lib, ke=P + 2) == ALIGN
+    assert fwd8(fa_lib, o=P) == INVALID                   # o overlaps the codes
+    assert fwd8(fa_lib, lse=FAR[0] + 256) == INVALID      # lse overlaps o
+    assert fwd8(fa_lib, B=1 << 16, H=1 << 16, Hkv=1, N=1 << 10) == UNSUPPORTED
 
 
 def dec(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=P, S=4, H=8, Hkv=8, D=128, BS=16, MB=4,

@@ -1,0 +1,106 @@
+"""GPU parity of the block-scaled FP8 path, through the C ABI.
+
+fa_quant_fp8 must reproduce the oracle's E4M3 codes and block exponents bit
+for bit (both layouts, ragged N, every input type, blocks spanning many
+binades).  fa_fwd_fp8 runs on those codes and is compared with the fp64
+oracle's attention on the dequantised values, which the oracle computes from
+its own quantisation of the same inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_12_amd as fa
+import oracle
+from exact_attention_12_amd import inputs
+from gpu_util import FP8_TOL, errors, progress
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    progress("start " + request.node.nodeid)
+    yield
+
+
+def spread(cfg_seed, shape, dtype):
+    """N(0,1) rows with per-block magnitudes spread over 2^-20 .. 2^11."""
+    x = inputs.normal(cfg_seed, shape, 1.0, torch.float32)
+    N = shape[2]
+    f = np.exp2(np.random.default_rng(cfg_seed + 1).integers(-20, 12, size=(shape[0], shape[1], (N + 127) // 128)))
+    f = torch.from_numpy(f).float().repeat_interleave(128, dim=2)[:, :, :N, None]
+    return (x * f).to(dtype)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("N,d", [(300, 128), (64, 64), (1, 128), (200, 64)])
+def test_quant_bit_exact(gpu, fa_lib, dt, layout, N, d):
+    dtype = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
+    x = spread(4000 + N, (2, 3, N, d), dtype)
+    x[0, 0, :min(N, 128)] = 0  # an all-zero block
+    progress("fa_quant_fp8 %s layout %d N=%d d=%d" % (dt, layout, N, d))
+    codes, exps = fa.quant_fp8(x.to(gpu), layout)
+    torch.cuda.synchronize()
+    rc, re = oracle.quant_fp8(x, layout)
+    got = codes.cpu().numpy()[:rc.size].reshape(rc.shape)
+    assert np.array_equal(exps.cpu().numpy(), re)
+    assert np.array_equal(got, rc), int((got != rc).sum())
+
+
+def fp8_inputs(cfg):
+    q, k, v = inputs.fwd_inputs(cfg)
+    return q, k, v
+
+
+def run_fp8(cfg, dev, rows=None, label=""):
+    q, k, v = fp8_inputs(cfg)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = float(np.float32(cfg.scale))
+    progress("fa_fwd_fp8 %s B=%d H=%d Hkv=%d N=%d causal=%d" % (label, B, H, Hkv, N, cfg.causal))
+    q8, qe = fa.quant_fp8(q.to(dev), 0)
+    k8, ke = fa.quant_fp8(k.to(dev), 0)
+    v8, ve = fa.quant_fp8(v.to(dev), 1)
+    o, lse = fa.forward_fp8(q8, k8, v8, qe, ke, ve, B, H, Hkv, N, d, scale, cfg.causal)
+    torch.cuda.synchronize()
+    deq = []
+    for t, layout in ((q, 0), (k, 0), (v, 1)):
+        c, e = oracle.quant_fp8(t, layout)
+        deq.append(torch.from_numpy(oracle.dequant_fp8(c, e, t.shape[0], t.shape[1], N, d, layout)))
+    o_ref, l_ref = oracle.attention(deq[0], deq[1], deq[2], scale, cfg.causal, rows=rows)
+    o_abs, _ = oracle.attention(deq[0], deq[1], deq[2].abs(), scale, cfg.causal, rows=rows)
+    bound = FP8_TOL["rel"] * o_abs + FP8_TOL["abs"]
+    og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    if rows is not None:
+        og, lg = og[:, :, rows], lg[:, :, rows]
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    omax, omean = errors(og, o_ref)
+    lmax, _ = errors(lg, l_ref)
+    ratio = float((np.abs(og - o_ref) / bound).max())
+    progress("%s max|dO|=%.3g mean|dO|=%.3g max|dlse|=%.3g max |dO|/bound=%.3f" % (
+        label, omax, omean, lmax, ratio))
+    assert ratio <= 1.0, (label, ratio)
+    assert lmax <= FP8_TOL["lse_max"], (label, lmax)
+    return o, lse
+
+
+@pytest.mark.parametrize("N,causal,H,Hkv", [
+    (333, True, 2, 2), (333, False, 2, 2), (64, True, 1, 1), (1, False, 1, 1), (129, True, 4, 2),
+    (1000, True, 8, 1), (512, False, 2, 2)])
+def test_fwd_fp8_shapes(gpu, fa_lib, N, causal, H, Hkv):
+    cfg = inputs.FwdConfig(70, 2, H, N, 128, torch.bfloat16, causal, 1.0, "", Hkv=Hkv)
+    run_fp8(cfg, gpu, label="N%d causal%d H%d Hkv%d" % (N, causal, H, Hkv))
+
+
+def test_fwd_fp8_deterministic(gpu, fa_lib):
+    cfg = inputs.FwdConfig(71, 1, 2, 700, 128, torch.bfloat16, True, 1.0, "")
+    a = run_fp8(cfg, gpu, label="det a")
+    b = run_fp8(cfg, gpu, label="det b")
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_fwd_fp8_headline_sampled(gpu, fa_lib):
+    cfg = inputs.FWD_CONFIGS[3]
+    run_fp8(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5), label=cfg.name)
