@@ -11,6 +11,7 @@ and widened exactly inside the C code.
 
 Functions (each cites the page passages it follows in ``oracle.c``):
   attention(q, k, v, scale, causal, rows=None)        dense definition
+  attention_ext(q, k, v, scale, causal, window, mask)  rectangular, windowed, masked
   probs(q, k, scale, causal)                          the full P matrix
   tiled_fa1 / tiled_fa2(q, k, v, scale, causal, Br, Bc)
                                                       the online recurrence in
@@ -71,6 +72,9 @@ def _load():
                                                     vp, vp, vp, vp, vp, i]
     lib.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, d, i, vp, i64, vp, i64,
                                          vp, vp, vp, vp, i]
+    lib.oracle_attention_ext.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, d, i, i, i, vp, i64, i64,
+                                         vp, vp, i]
+    lib.oracle_attention_ext.restype = i
     lib.oracle_e4m3_encode.argtypes = [vp, i64, vp]
     lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
     lib.oracle_fp8_codes_len.argtypes = [i, i, i, i, i]
@@ -151,6 +155,44 @@ def attention(q, k, v, scale, causal, rows=None, nthreads=None):
                                   None if rarr is None else _p(rarr), R, _p(o), _p(lse),
                                   nthreads or default_threads())
     _check(st, "oracle_attention")
+    return o, lse
+
+
+def attention_ext(q, k, v, scale, causal=False, window=(-1, -1), mask=None, nthreads=None):
+    """Attention of q [B, H, Nq, d] over k, v [B, Hkv, Nk, d] with a bottom-right aligned
+    causal mask, a (left, right) window around the diagonal i + Nk - Nq (-1 = unbounded)
+    and an optional boolean mask broadcastable to [B, H, Nq, Nk] (True = admissible).
+
+    Returns (o [B, H, Nq, d], lse [B, H, Nq]) fp64; rows with no admissible key get
+    o = 0 and lse = -inf.
+    """
+    qt, code = _host(q)
+    kt, c2 = _host(k)
+    vt, c3 = _host(v)
+    if not (code == c2 == c3) or qt.dim() != 4 or kt.shape != vt.shape or kt.dim() != 4:
+        raise ValueError("q [B, H, Nq, d] and k, v one [B, Hkv, Nk, d] shape, one dtype")
+    B, H, Nq, d = qt.shape
+    Hkv, Nk = kt.shape[1], kt.shape[2]
+    if kt.shape[0] != B or kt.shape[3] != d or H % Hkv != 0:
+        raise ValueError("k, v must be [B, Hkv, Nk, d] with Hkv dividing H")
+    m, sb, sh = None, 0, 0
+    if mask is not None:
+        mt = torch.as_tensor(mask).detach().cpu().to(torch.uint8)
+        while mt.dim() < 4:
+            mt = mt.unsqueeze(0)
+        Bm, Hm = mt.shape[0], mt.shape[1]   # 1 (broadcast) or B / H
+        if mt.shape[2:] != (Nq, Nk) or Bm not in (1, B) or Hm not in (1, H):
+            raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
+        m = mt.contiguous()
+        sb = 0 if Bm == 1 else Hm * Nq * Nk
+        sh = 0 if Hm == 1 else Nq * Nk
+    o = np.empty((B, H, Nq, d), dtype=np.float64)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    st = _load().oracle_attention_ext(_p(qt), _p(kt), _p(vt), code, B, H, Hkv, Nq, Nk, d,
+                                      float(scale), int(bool(causal)), int(window[0]),
+                                      int(window[1]), None if m is None else _p(m), sb, sh,
+                                      _p(o), _p(lse), nthreads or default_threads())
+    _check(st, "oracle_attention_ext")
     return o, lse
 
 

@@ -981,3 +981,99 @@ int oracle_dequant_fp8(const uint8_t *codes, const int32_t *exps, int B, int H, 
                           exps[bh * nblk + i / 128]);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Attention with general masks                                         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [YJ] 11.3 passes either is_causal or an explicit boolean attn_mask (True =
+ * the pair takes part); [YJ] 11.6 names sliding-window attention.  The
+ * admissible keys of query row i (0 <= i < Nq) over Nk keys are
+ *     A_i = { j < Nk : (!causal  or j <= i + off)
+ *                     and (wl < 0 or j >= i + off - wl)
+ *                     and (wr < 0 or j <= i + off + wr)
+ *                     and (!mask or mask[i][j] != 0) },   off = Nk - Nq,
+ * i.e. a causal mask aligned to the bottom-right corner when Nq != Nk (the
+ * last query is the last key, as for new tokens appended to a context), and
+ * a window of wl keys to the left and wr keys to the right of that
+ * diagonal (a negative bound is unbounded).  mask is uint8 [.., Nq, Nk] at
+ * element offset b * mask_sb + h * mask_sh (a zero stride broadcasts).
+ * O_i = softmax over A_i of scale q_i . k_j applied to V; an empty A_i gives
+ * O_i = 0 and lse_i = -inf.
+ */
+typedef struct {
+    const void *q, *k, *v;
+    int dtype;
+    int B, H, Hkv, Nq, Nk, d;
+    double scale;
+    int causal, wl, wr;
+    const uint8_t *mask;
+    int64_t msb, msh;
+    double *o, *lse;
+} or_ext_ctx;
+
+static int or_ext_admissible(const or_ext_ctx *x, int64_t b, int64_t h, int64_t i, int64_t j)
+{
+    int64_t off = (int64_t)x->Nk - x->Nq;
+    if (x->causal && j > i + off) return 0;
+    if (x->wl >= 0 && j < i + off - x->wl) return 0;
+    if (x->wr >= 0 && j > i + off + x->wr) return 0;
+    if (x->mask && !x->mask[b * x->msb + h * x->msh + i * x->Nk + j]) return 0;
+    return 1;
+}
+
+typedef struct {
+    const void *v;
+    int dtype;
+    int64_t base;
+    int d;
+    const int64_t *idx; /* admissible key of each position */
+} or_ext_v;
+
+static double or_ext_value(const void *ctx, int64_t j, int c)
+{
+    const or_ext_v *ev = (const or_ext_v *)ctx;
+    return or_load(ev->v, ev->dtype, ev->base + ev->idx[j] * ev->d + c);
+}
+
+static void or_ext_item(void *vctx, int64_t item, double *scratch)
+{
+    const or_ext_ctx *x = (const or_ext_ctx *)vctx;
+    int64_t i = item % x->Nq, bh = item / x->Nq;
+    int64_t b = bh / x->H, h = bh % x->H;
+    int64_t qb = bh * (int64_t)x->Nq * x->d;
+    int64_t kb = (b * x->Hkv + h / (x->H / x->Hkv)) * (int64_t)x->Nk * x->d;
+    double *s = scratch;
+    int64_t *idx = (int64_t *)(scratch + x->Nk);
+    int64_t n = 0;
+    for (int64_t j = 0; j < x->Nk; ++j) {
+        if (!or_ext_admissible(x, b, h, i, j)) continue;
+        double dot = 0.0;
+        for (int c = 0; c < x->d; ++c)
+            dot += or_load(x->q, x->dtype, qb + i * x->d + c) * or_load(x->k, x->dtype, kb + j * x->d + c);
+        s[n] = x->scale * dot;
+        idx[n] = j;
+        ++n;
+    }
+    or_ext_v ev = { x->v, x->dtype, kb, x->d, idx };
+    x->lse[item] = or_softmax_row(s, n, x->d, or_ext_value, &ev, x->o + item * x->d);
+}
+
+/*
+ * q [B, H, Nq, d]; k, v [B, Hkv, Nk, d]; o [B, H, Nq, d] and lse [B, H, Nq]
+ * fp64.  mask may be NULL.
+ */
+int oracle_attention_ext(const void *q, const void *k, const void *v, int dtype, int B, int H,
+                         int Hkv, int Nq, int Nk, int d, double scale, int causal, int wl, int wr,
+                         const uint8_t *mask, int64_t mask_sb, int64_t mask_sh, double *o,
+                         double *lse, int nthreads)
+{
+    if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return -1;
+    if (Hkv < 1 || H % Hkv != 0 || or_elem_bytes(dtype) == 0) return -1;
+    if (mask && (mask_sb < 0 || mask_sh < 0)) return -1;
+    or_ext_ctx x = { q, k, v, dtype, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0,
+                     wl, wr, mask, mask_sb, mask_sh, o, lse };
+    /* scratch: Nk scores + Nk key indices (int64 stored in doubles' space) */
+    return or_parallel(or_ext_item, &x, (int64_t)B * H * Nq, 2 * (int64_t)Nk, nthreads);
+}

@@ -17,7 +17,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_decode.py",
-              "tests/test_oracle_tiling.py", "tests/test_oracle_bwd.py", "tests/test_oracle_fp8.py"]
+              "tests/test_oracle_tiling.py", "tests/test_oracle_bwd.py", "tests/test_oracle_fp8.py",
+              "tests/test_oracle_ext.py"]
 
 # (name, text in oracle.c, replacement); the text must occur in the source
 MUTATIONS = [
@@ -111,6 +112,21 @@ MUTATIONS = [
     ("fp8_tile_layout_swapped",
      "return ((bh * T + i / 64) * d + c) * 64 + (i % 64);",
      "return ((bh * T + i / 64) * 64 + (i % 64)) * d + c;"),
+    ("ext_causal_offset_sign",
+     "if (x->causal && j > i + off) return 0;",
+     "if (x->causal && j > i - off) return 0;"),
+    ("ext_window_left_off_by_one",
+     "if (x->wl >= 0 && j < i + off - x->wl) return 0;",
+     "if (x->wl >= 0 && j <= i + off - x->wl) return 0;"),
+    ("ext_window_right_ignored",
+     "if (x->wr >= 0 && j > i + off + x->wr) return 0;",
+     ""),
+    ("ext_mask_transposed",
+     "x->mask[b * x->msb + h * x->msh + i * x->Nk + j]",
+     "x->mask[b * x->msb + h * x->msh + j * x->Nq + i]"),
+    ("ext_mask_head_stride_dropped",
+     "x->mask[b * x->msb + h * x->msh + i * x->Nk + j]",
+     "x->mask[b * x->msb + i * x->Nk + j]"),
     ("bwd_group_mapping",
      "for (int64_t h = g * group; h < (g + 1) * group; ++h) {",
      "for (int64_t h = g; h < x->H; h += x->Hkv) {"),
