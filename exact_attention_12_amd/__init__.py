@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "FA_F32", "FA_BF16", "FA_F16", "FA_DECODE_PARTITION_TOKENS", "FAError", "fa_fwd_gqa",
-    "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_quant_fp8",
+    "fa_fwd", "fa_fwd_ext", "forward_ext", "fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_quant_fp8",
     "fa_fwd_fp8", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror", "forward",
     "backward", "quant_fp8", "forward_fp8", "paged_decode", "lib_path", "load_library",
     "FA_FP8_BLOCK_ROWS",
@@ -64,6 +64,9 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_gqa.restype = i
+    i64 = ctypes.c_int64
+    lib.fa_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, i64, i64, i, vp]
+    lib.fa_fwd_ext.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -138,6 +141,21 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype=None, stre
                                    int(dtype), _stream(stream))
     if st != 0:
         raise FAError(st, "fa_fwd_gqa")
+
+
+def fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window_left=-1,
+               window_right=-1, mask=None, mask_stride_b=0, mask_stride_h=0, dtype=None,
+               stream=None):
+    """C entry point ``fa_fwd_ext``: rectangular / windowed / boolean-masked forward."""
+    if dtype is None:
+        dtype = _dtype_code(q.dtype)
+    st = load_library().fa_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                   int(Hkv), int(Nq), int(Nk), int(d), float(scale),
+                                   int(bool(causal)), int(window_left), int(window_right),
+                                   _ptr(mask), int(mask_stride_b), int(mask_stride_h), int(dtype),
+                                   _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_fwd_ext")
 
 
 def fa_bwd_workspace_size(B, H, N) -> int:
@@ -246,6 +264,36 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     else:
         fa_fwd_gqa(q, k, v, out, lse, B, H, Hkv, N, d, scale, causal, stream=stream)
     return out, lse
+
+
+def forward_ext(q, k, v, scale=None, causal=False, window=(-1, -1), mask=None, stream=None):
+    """Allocate o, lse and run ``fa_fwd_ext``: q [B, H, Nq, d], k, v [B, Hkv, Nk, d], a
+    bottom-right aligned causal mask, a (left, right) window (-1 = unbounded) and an
+    optional boolean / uint8 mask broadcastable to [B, H, Nq, Nk] (True = takes part)."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d or H % Hkv != 0:
+        raise ValueError("k, v must be [B, Hkv, Nk, d] with Hkv dividing H")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sb = sh = 0
+    if mask is not None:
+        m = mask
+        while m.dim() < 4:
+            m = m.unsqueeze(0)
+        if m.shape[2:] != (Nq, Nk) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
+            raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
+        mask = m.to(torch.uint8).contiguous()
+        sb = 0 if m.shape[0] == 1 else m.shape[1] * Nq * Nk
+        sh = 0 if m.shape[1] == 1 else Nq * Nk
+        _check_dev("mask", mask, torch.uint8)
+    o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window[0], window[1], mask,
+               sb, sh, stream=stream)
+    return o, lse
 
 
 def backward(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):

@@ -69,13 +69,29 @@ template <typename T, int D> struct FwdCfg {
 // softmax step in the kernel): 2^14, representable in every input type.
 constexpr float kPMax = 16384.0f;
 
-template <typename T, int D, bool CAUSAL>
+// General masks (rectangular, windowed, boolean; the EXT kernels).  Query row
+// i of Nq rows sees key j < Nk iff  i + off - wl <= j <= i + off + wr  and, with
+// a mask, mask[i][j] != 0; off = Nk - Nq aligns the diagonal to the
+// bottom-right corner.  Unbounded sides come in as bounds beyond the key range.
+struct FwdExt {
+    int Nk;               // keys (the kernel's N counts query rows)
+    int off, wl, wr;      // diagonal offset and window, all pre-clamped by the host
+    const uint8_t *mask;  // uint8 [.., Nq, Nk] or null
+    int64_t msb, msh;     // element strides of the mask between batches and heads
+};
+
+// EXT: 0 = square path (N queries and keys, optional top-left causal mask),
+// 1 = general ranges (rectangular / windowed / bottom-right causal), 2 = 1
+// plus a boolean mask.
+template <typename T, int D, bool CAUSAL, int EXT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(FwdCfg<T, D>::WPE, FwdCfg<T, D>::WPE)))
 void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                    float *__restrict__ O, float *__restrict__ LSE, int N, int num_qtiles,
-                   float scale, int H, int group)
+                   float scale, int H, int group, FwdExt ext)
 {
+    static_assert(EXT == 0 || !CAUSAL, "general masks fold causality into the window");
+    const int NK = EXT ? ext.Nk : N;  // keys
     using C = FwdCfg<T, D>;
     using M = Mma<T>;
     using frag = typename M::frag;
@@ -105,7 +121,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // Q, O, lse: head bh = b*H + h.  K, V: kv head b*(H/group) + h/group
     // (group query heads share one kv head; group = 1 is multi-head attention).
     const int64_t head = (int64_t)bh * N * D;
-    const int64_t kv_head = ((int64_t)(bh / H) * (H / group) + (bh % H) / group) * N * D;
+    const int64_t kv_head = ((int64_t)(bh / H) * (H / group) + (bh % H) / group) * NK * D;
     const T *Qh = Q + head;
     const T *Kh = K + kv_head;
     const T *Vh = V + kv_head;
@@ -131,7 +147,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         ld_row[i] = q / C::CPR;
         ld_off[i] = (ld_row[i] * D + ((q % C::CPR) ^ swz<C::CPR, C::ES>(ld_row[i])) * C::VEC) * C::ES;
     }
-    const int head_bytes = N * C::ROWB;
+    const int head_bytes = NK * C::ROWB;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)Kh, 0, head_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)Vh, 0, head_bytes, kBufferFlags);
     auto load_tile = [&](int j, int buf) {
@@ -139,7 +155,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         char *kd = smem + buf * C::STAGEB;
         char *vd = kd + C::TILEB;
         const int soff = k0 * C::ROWB;
-        if (k0 + C::BC <= N) {
+        if (k0 + C::BC <= NK) {
 #pragma unroll
             for (int i = 0; i < C::NLD_W; ++i) {
                 const int I = wave * C::NLD_W + i;
@@ -151,7 +167,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 #pragma unroll
             for (int i = 0; i < C::NLD_W; ++i) {
                 const int I = wave * C::NLD_W + i;
-                const int over = k0 + ld_row[i] - (N - 1);
+                const int over = k0 + ld_row[i] - (NK - 1);
                 const int off = over > 0 ? ld_off[i] - over * C::ROWB : ld_off[i];
                 buffer_load_lds16(krs, kd + I * 1024, off, soff);
                 buffer_load_lds16(vrs, vd + I * 1024, off, soff);
@@ -220,18 +236,67 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     };
     // Masks: keys >= N (ragged tail) and, causal, keys > query row.  Key
     // k0 + kb*32 + acc_row(r, h) is visible iff acc_row(r, 0) <= lim[kb].
-    auto limits = [&](int k0, int (&lim)[C::NKB]) {
-        const int last = CAUSAL ? min(qrow, N - 1) : N - 1;
+    // General masks add a lower bound lo[kb] (visible iff acc_row(r, 0) >=
+    // lo[kb]) and the mask bytes of the lane's 16 keys per block.
+    auto limits = [&](int k0, int (&lim)[C::NKB], int (&lo)[C::NKB]) {
+        int last = CAUSAL ? min(qrow, N - 1) : N - 1;
+        int first = 0;
+        if constexpr (EXT != 0) {
+            const int qr = min(qrow, N - 1);  // rows past the end behave like row N-1
+            last = min(qr + ext.off + ext.wr, NK - 1);
+            first = qr + ext.off - ext.wl;
+        }
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) lim[kb] = last - k0 - kb * 32 - 4 * h;
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            lim[kb] = last - k0 - kb * 32 - 4 * h;
+            lo[kb] = first - k0 - kb * 32 - 4 * h;
+        }
     };
-    auto apply_mask = [&](f32x16 (&s)[C::NKB], const int (&lim)[C::NKB]) {
+    // mask bytes of keys k0 + kb*32 + 8g + 4h + 0..3, one dword per (kb, g);
+    // reads past the mask (ragged tail) return 0 = masked
+    const uint8_t *mbase = nullptr;
+    if constexpr (EXT == 2) mbase = ext.mask + (int64_t)(bh / H) * ext.msb + (int64_t)(bh % H) * ext.msh;
+    const __amdgpu_buffer_rsrc_t mrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)mbase, 0, EXT == 2 ? N * NK : 0, kBufferFlags);
+    int mrow = 0;
+    auto load_mask = [&](int k0, uint32_t (&mw)[C::NKB][4]) __attribute__((always_inline)) {
+        if constexpr (EXT == 2) {
+            const int base = mrow + k0 + 4 * h;
+            if ((NK & 3) == 0) {
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        mw[kb][g] = __builtin_amdgcn_raw_buffer_load_b32(mrs, base + kb * 32 + 8 * g, 0, 0);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        uint32_t w = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(mrs, base + kb * 32 + 8 * g + e, 0, 0)
+                                 << (8 * e);
+                        mw[kb][g] = w;
+                    }
+            }
+        }
+    };
+    auto apply_mask = [&](f32x16 (&s)[C::NKB], const int (&lim)[C::NKB], const int (&lo)[C::NKB],
+                          const uint32_t (&mw)[C::NKB][4]) {
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (acc_row(r, 0) > lim[kb]) s[kb][r] = -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+                bool off_ = acc_row(r, 0) > lim[kb];
+                if constexpr (EXT != 0) off_ = off_ || acc_row(r, 0) < lo[kb];
+                if constexpr (EXT == 2) off_ = off_ || ((mw[kb][r / 4] >> (8 * (r % 4))) & 0xffu) == 0;
+                if (off_) s[kb][r] = -INFINITY;
+            }
     };
+    // first and last key tiles of this wave's rows (general masks)
+    int jw_beg = 0, jw_end = 0;
     // Move the reference to the row max of this tile where that is larger,
     // rescaling what was accumulated against the old reference.
     auto rebase = [&](const f32x16 (&s)[C::NKB]) {
@@ -244,7 +309,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         const float m_new = fmaxf(m_ref, mx);
         const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
         const float mc_new = m_safe * c;
-        const float alpha = exp2_hw(mc_ref - mc_new);  // e^(scale*(m_old - m_new)); 0 at start
+        // a row that saw no key yet (m_ref = -inf) has nothing to rescale
+        const float alpha = (EXT != 0 && m_ref == -INFINITY) ? 0.f : exp2_hw(mc_ref - mc_new);  // e^(scale*(m_old - m_new)); 0 at start
         l_run *= alpha;
         l_hat *= alpha;
 #pragma unroll
@@ -274,12 +340,24 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         const char *Ks = smem + STAGE * C::STAGEB;
         const char *Vs = Ks + C::TILEB;
 
+        if (EXT != 0 && (j < jw_beg || j >= jw_end)) {
+            // no row of this wave sees a key of this tile
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            return;
+        }
+        uint32_t mw[C::NKB][4];
+        load_mask(k0, mw);
         f32x16 s[C::NKB];
         qk(Ks, s);
-        const bool need_mask = (k0 + C::BC > N) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
-        int lim[C::NKB];
-        limits(k0, lim);
-        if (need_mask) apply_mask(s, lim);
+        bool need_mask = (k0 + C::BC > NK) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
+        if constexpr (EXT == 1)
+            need_mask = k0 < min(wq_hi, N - 1) + ext.off - ext.wl ||
+                        k0 + C::BC - 1 > min(wq_lo + ext.off + ext.wr, NK - 1);
+        if constexpr (EXT == 2) need_mask = true;
+        int lim[C::NKB], lo[C::NKB];
+        limits(k0, lim, lo);
+        if (need_mask) apply_mask(s, lim, lo, mw);
 
         // Lazy reference max.  The probabilities are taken relative to a
         // reference m_ref instead of the running max: exp(s - m) =
@@ -290,11 +368,13 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         // only if some lane's sum exceeds kPMax = 2^14 (which bounds every
         // probability, keeping it representable even in fp16) recompute the
         // tile's scores and move the reference.
-        if (j == 0) rebase(s);
+        // General masks: a row may see no key of its first tiles, so the
+        // reference is (re)set while any row of the wave has none yet.
+        if (EXT == 0 ? j == 0 : __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0) rebase(s);
         float rs = exponentiate(s);
-        if (j != 0 && __builtin_amdgcn_ballot_w64(!(rs <= kPMax)) != 0) {
+        if ((EXT != 0 || j != 0) && __builtin_amdgcn_ballot_w64(!(rs <= kPMax)) != 0) {
             qk(Ks, s);
-            if (need_mask) apply_mask(s, lim);
+            if (need_mask) apply_mask(s, lim, lo, mw);
             rebase(s);
             rs = exponentiate(s);
         }
@@ -360,8 +440,23 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         else
             qf[st] = frag{};
     }
-    const int kend = CAUSAL ? min(N, q0 + C::BR) : N;  // keys [0, kend) can be seen
-    ntiles = (kend + C::BC - 1) / C::BC;
+    int kend = CAUSAL ? min(N, q0 + C::BR) : N;  // keys [0, kend) can be seen
+    int jbeg = 0;
+    if constexpr (EXT != 0) {
+        // keys [kbeg, kend) can be seen by the workgroup's rows, and
+        // [kw_beg, kw_end) by this wave's
+        const int q_last = min(q0 + C::BR, N) - 1;
+        const int kbeg = max(0, q0 + ext.off - ext.wl);
+        kend = min(NK, q_last + ext.off + ext.wr + 1);
+        jbeg = kbeg / C::BC;
+        const int w_last = min(wq_hi, N - 1);
+        const int kw_beg = max(0, wq_lo + ext.off - ext.wl);
+        const int kw_end = min(NK, w_last + ext.off + ext.wr + 1);
+        jw_beg = kw_beg / C::BC;
+        jw_end = (wq_lo < N && kw_end > kw_beg) ? (kw_end + C::BC - 1) / C::BC : 0;
+        mrow = min(qrow, N - 1) * NK;
+    }
+    ntiles = kend > jbeg * C::BC ? (kend + C::BC - 1) / C::BC : jbeg;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
     m_ref = -INFINITY;
@@ -369,14 +464,18 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     l_run = 0.f;
     l_hat = 0.f;
 
-    load_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    if (jbeg < ntiles) {
+        load_tile(jbeg, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
 
     // Causal: this wave's rows see no key of tiles j >= nt_w; those tiles are
     // still loaded for the other waves (same barrier count for every wave).
+    // General masks: every tile of the workgroup's range runs through tile(),
+    // which skips the arithmetic for the wave's tiles outside [jw_beg, jw_end).
     const int nt_w = CAUSAL ? min(ntiles, wq_hi / C::BC + 1) : ntiles;
-    int j = 0;
+    int j = jbeg;
     for (; j + 1 < nt_w; j += 2) {
         tile(j, std::integral_constant<int, 0>{});
         tile(j + 1, std::integral_constant<int, 1>{});
@@ -386,7 +485,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         ++j;
     }
     for (; j < ntiles; ++j) {
-        if (j + 1 < ntiles) load_tile(j + 1, (j + 1) & 1);
+        if (j + 1 < ntiles) load_tile(j + 1, (j + 1 - jbeg) & 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
@@ -397,7 +496,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // combination of the value rows with consistently rounded weights; lse
     // uses the unrounded fp32 sum.
     const float l_tot = halves_sum(l_run);
-    const float inv = 1.f / halves_sum(l_hat);
+    float inv = 1.f / halves_sum(l_hat);
+    if (EXT != 0 && !(l_tot > 0.f)) inv = 0.f;  // no visible key: O = 0, lse = -inf
     if (qrow < N) {
         float *orow = O + head + (int64_t)qrow * D;
 #pragma unroll
@@ -420,8 +520,26 @@ static hipError_t launch_fwd(const void *q, const void *k, const void *v, float 
     using C = FwdCfg<T, D>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const int64_t grid = (int64_t)B * H * (CAUSAL ? (nqt + 1) / 2 : nqt);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, o, lse, N, nqt, scale, H, H / Hkv);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 0>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, o, lse, N, nqt, scale, H, H / Hkv,
+                       FwdExt{N, 0, 0, 0, nullptr, 0, 0});
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_ext(const void *q, const void *k, const void *v, float *o, float *lse,
+                                 int B, int H, int Hkv, int Nq, float scale, const FwdExt &ext,
+                                 hipStream_t stream)
+{
+    using C = FwdCfg<T, D>;
+    const int nqt = (Nq + C::BR - 1) / C::BR;
+    const int64_t grid = (int64_t)B * H * nqt;
+    if (ext.mask)
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, 2>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                           (const T *)q, (const T *)k, (const T *)v, o, lse, Nq, nqt, scale, H, H / Hkv, ext);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, 1>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                           (const T *)q, (const T *)k, (const T *)v, o, lse, Nq, nqt, scale, H, H / Hkv, ext);
     return hipGetLastError();
 }
 
@@ -452,6 +570,32 @@ hipError_t fwd_dispatch(const void *q, const void *k, const void *v, float *o, f
         return d == 64
                    ? launch_fwd_c<_Float16, 64>(q, k, v, o, lse, B, H, Hkv, N, scale, causal, stream)
                    : launch_fwd_c<_Float16, 128>(q, k, v, o, lse, B, H, Hkv, N, scale, causal, stream);
+    }
+}
+
+// General masks.  Arguments validated by the caller: Nq, Nk >= 1; wl, wr are
+// the window bounds (< 0 = unbounded); causal limits the right bound to 0.
+hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
+                            int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int wl,
+                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int dtype,
+                            hipStream_t stream)
+{
+    // bounds beyond Nq + Nk are unbounded; keep every sum inside int
+    const int big = Nq + Nk;
+    int r = wr < 0 ? big : min(wr, big);
+    if (causal) r = min(r, 0);
+    const int l = wl < 0 ? big : min(wl, big);
+    const FwdExt ext{Nk, Nk - Nq, l, r, mask, msb, msh};
+    switch (dtype) {
+    case 0:
+        return d == 64 ? launch_fwd_ext<float, 64>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream)
+                       : launch_fwd_ext<float, 128>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream);
+    case 1:
+        return d == 64 ? launch_fwd_ext<__bf16, 64>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream)
+                       : launch_fwd_ext<__bf16, 128>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream);
+    default:
+        return d == 64 ? launch_fwd_ext<_Float16, 64>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream)
+                       : launch_fwd_ext<_Float16, 128>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream);
     }
 }
 

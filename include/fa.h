@@ -112,6 +112,36 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse
                int Hkv, int N, int d, float scale, int causal, int dtype, void *stream);
 
 /*
+ * fa_fwd_ext -- fa_fwd_gqa with general masks: a different number of keys
+ * than queries, a causal mask aligned to the bottom-right corner, a sliding
+ * window and a boolean mask (youngju.dev section 11.3: is_causal or an
+ * explicit boolean attn_mask in which True marks a pair that takes part;
+ * section 11.6 names sliding-window attention).
+ *
+ *   q         : [B, H, Nq, d];  k, v : [B, Hkv, Nk, d];  o : [B, H, Nq, d]
+ *               fp32;  lse : [B, H, Nq] fp32.  Types and alignment as fa_fwd.
+ *   Query row i sees key j < Nk iff
+ *       (causal == 0 or j <= i + off)
+ *       and (window_left < 0 or j >= i + off - window_left)
+ *       and (window_right < 0 or j <= i + off + window_right)
+ *       and (mask == NULL or mask[b * mask_stride_b + h * mask_stride_h
+ *                                 + i * Nk + j] != 0),
+ *   with off = Nk - Nq: the last query row is aligned with the last key (new
+ *   tokens appended to a context).  Nq = Nk, causal, no window and no mask
+ *   is fa_fwd's causal mask.
+ *   mask      : uint8 (0 = masked), rows of Nk bytes per (b, h) slice at the
+ *               given element strides (0 broadcasts over that dimension), or
+ *               NULL.  Nq * Nk must stay below 2^31.
+ *   A row that sees no key gets o = 0 and lse = -inf.
+ * Every other argument and the error behaviour are those of fa_fwd_gqa; o
+ * and lse must not overlap q, k, v or the mask.
+ */
+int fa_fwd_ext(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
+               int Hkv, int Nq, int Nk, int d, float scale, int causal, int window_left,
+               int window_right, const uint8_t *mask, int64_t mask_stride_b, int64_t mask_stride_h,
+               int dtype, void *stream);
+
+/*
  * fa_bwd_workspace_size -- bytes of device workspace that fa_bwd needs: two
  * fp32 values per query row (D_i = dO_i . O_i and lse_i * log2 e),
  * 2 * B * H * N * 4 bytes rounded up to 256.  Returns 0 for invalid sizes.

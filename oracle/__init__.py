@@ -73,7 +73,7 @@ def _load():
     lib.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, d, i, vp, i64, vp, i64,
                                          vp, vp, vp, vp, i]
     lib.oracle_attention_ext.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, d, i, i, i, vp, i64, i64,
-                                         vp, vp, i]
+                                         vp, i64, vp, vp, i]
     lib.oracle_attention_ext.restype = i
     lib.oracle_e4m3_encode.argtypes = [vp, i64, vp]
     lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
@@ -158,13 +158,14 @@ def attention(q, k, v, scale, causal, rows=None, nthreads=None):
     return o, lse
 
 
-def attention_ext(q, k, v, scale, causal=False, window=(-1, -1), mask=None, nthreads=None):
+def attention_ext(q, k, v, scale, causal=False, window=(-1, -1), mask=None, rows=None,
+                  nthreads=None):
     """Attention of q [B, H, Nq, d] over k, v [B, Hkv, Nk, d] with a bottom-right aligned
     causal mask, a (left, right) window around the diagonal i + Nk - Nq (-1 = unbounded)
     and an optional boolean mask broadcastable to [B, H, Nq, Nk] (True = admissible).
 
-    Returns (o [B, H, Nq, d], lse [B, H, Nq]) fp64; rows with no admissible key get
-    o = 0 and lse = -inf.
+    Returns (o [B, H, R, d], lse [B, H, R]) fp64 for the R selected rows (all Nq if
+    rows is None); rows with no admissible key get o = 0 and lse = -inf.
     """
     qt, code = _host(q)
     kt, c2 = _host(k)
@@ -186,11 +187,17 @@ def attention_ext(q, k, v, scale, causal=False, window=(-1, -1), mask=None, nthr
         m = mt.contiguous()
         sb = 0 if Bm == 1 else Hm * Nq * Nk
         sh = 0 if Hm == 1 else Nq * Nk
-    o = np.empty((B, H, Nq, d), dtype=np.float64)
-    lse = np.empty((B, H, Nq), dtype=np.float64)
+    if rows is None:
+        rarr, R = None, Nq
+    else:
+        rarr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R = len(rarr)
+    o = np.empty((B, H, R, d), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
     st = _load().oracle_attention_ext(_p(qt), _p(kt), _p(vt), code, B, H, Hkv, Nq, Nk, d,
                                       float(scale), int(bool(causal)), int(window[0]),
                                       int(window[1]), None if m is None else _p(m), sb, sh,
+                                      None if rarr is None else _p(rarr), R,
                                       _p(o), _p(lse), nthreads or default_threads())
     _check(st, "oracle_attention_ext")
     return o, lse

@@ -1010,6 +1010,8 @@ typedef struct {
     int causal, wl, wr;
     const uint8_t *mask;
     int64_t msb, msh;
+    const int64_t *rows;
+    int64_t nrows;
     double *o, *lse;
 } or_ext_ctx;
 
@@ -1040,7 +1042,8 @@ static double or_ext_value(const void *ctx, int64_t j, int c)
 static void or_ext_item(void *vctx, int64_t item, double *scratch)
 {
     const or_ext_ctx *x = (const or_ext_ctx *)vctx;
-    int64_t i = item % x->Nq, bh = item / x->Nq;
+    int64_t r = item % x->nrows, bh = item / x->nrows;
+    int64_t i = x->rows ? x->rows[r] : r;
     int64_t b = bh / x->H, h = bh % x->H;
     int64_t qb = bh * (int64_t)x->Nq * x->d;
     int64_t kb = (b * x->Hkv + h / (x->H / x->Hkv)) * (int64_t)x->Nk * x->d;
@@ -1061,19 +1064,24 @@ static void or_ext_item(void *vctx, int64_t item, double *scratch)
 }
 
 /*
- * q [B, H, Nq, d]; k, v [B, Hkv, Nk, d]; o [B, H, Nq, d] and lse [B, H, Nq]
- * fp64.  mask may be NULL.
+ * q [B, H, Nq, d]; k, v [B, Hkv, Nk, d]; mask may be NULL.  rows selects the
+ * query rows to evaluate (NULL: all Nq); o [B, H, nrows, d] and
+ * lse [B, H, nrows] fp64.
  */
 int oracle_attention_ext(const void *q, const void *k, const void *v, int dtype, int B, int H,
                          int Hkv, int Nq, int Nk, int d, double scale, int causal, int wl, int wr,
-                         const uint8_t *mask, int64_t mask_sb, int64_t mask_sh, double *o,
-                         double *lse, int nthreads)
+                         const uint8_t *mask, int64_t mask_sb, int64_t mask_sh,
+                         const int64_t *rows, int64_t nrows, double *o, double *lse, int nthreads)
 {
     if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return -1;
     if (Hkv < 1 || H % Hkv != 0 || or_elem_bytes(dtype) == 0) return -1;
     if (mask && (mask_sb < 0 || mask_sh < 0)) return -1;
+    if (!rows) nrows = Nq;
+    if (nrows < 1) return -1;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= Nq) return -1;
     or_ext_ctx x = { q, k, v, dtype, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0,
-                     wl, wr, mask, mask_sb, mask_sh, o, lse };
+                     wl, wr, mask, mask_sb, mask_sh, rows, nrows, o, lse };
     /* scratch: Nk scores + Nk key indices (int64 stored in doubles' space) */
-    return or_parallel(or_ext_item, &x, (int64_t)B * H * Nq, 2 * (int64_t)Nk, nthreads);
+    return or_parallel(or_ext_item, &x, (int64_t)B * H * nrows, 2 * (int64_t)Nk, nthreads);
 }

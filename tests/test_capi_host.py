@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_exports_every_declared_function(fa_lib):
     names = declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_fwd", "fa_fwd_fp8",
-                     "fa_fwd_gqa", "fa_paged_decode", "fa_paged_decode_workspace_size",
+    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_fwd", "fa_fwd_ext",
+                     "fa_fwd_fp8", "fa_fwd_gqa", "fa_paged_decode", "fa_paged_decode_workspace_size",
                      "fa_quant_fp8", "fa_strerror"]
     for n in names:
         assert hasattr(fa_lib, n), n
@@ -147,6 +147,26 @@ def test_bwd_workspace_size(fa_lib):
     assert fa.fa_bwd_workspace_size(1, 1, 3) == 256
     assert fa.fa_bwd_workspace_size(0, 1, 3) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 0) == 0
+
+
+def fext(lib, q=P, k=P, v=P, o=FAR[0], lse=FAR[1], B=1, H=2, Hkv=1, Nq=10, Nk=30, d=64,
+         scale=0.125, causal=1, wl=-1, wr=-1, mask=None, sb=0, sh=0, dtype=1):
+    return lib.fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, wl, wr, mask, sb, sh,
+                          dtype, None)
+
+
+def test_fwd_ext_validation(fa_lib):
+    assert fext(fa_lib, q=0) == INVALID
+    assert fext(fa_lib, Nq=0) == INVALID
+    assert fext(fa_lib, Nk=-3) == INVALID
+    assert fext(fa_lib, Hkv=3) == INVALID
+    assert fext(fa_lib, mask=FAR[2], sb=-1) == INVALID
+    assert fext(fa_lib, dtype=4) == INVALID
+    assert fext(fa_lib, d=80) == UNSUPPORTED
+    assert fext(fa_lib, mask=FAR[2], Nq=1 << 16, Nk=1 << 16) == UNSUPPORTED  # mask slice >= 2^31
+    assert fext(fa_lib, k=P + 4) == ALIGN
+    assert fext(fa_lib, o=P) == INVALID                 # o overlaps q
+    assert fext(fa_lib, o=FAR[2], mask=FAR[2] + 64) == INVALID  # o overlaps the mask
 
 
 def quant(lib, x=P, dtype=1, B=1, H=2, N=100, d=128, layout=0, codes=FAR[0], exps=FAR[1]):

@@ -1,0 +1,129 @@
+"""GPU parity of fa_fwd_ext (rectangular, windowed, boolean-masked) against the
+fp64 oracle, through the C ABI.
+
+Rows that see no key must come back as o = 0 and lse = -inf exactly; the
+others meet the forward's bar for their input type.  Full comparison on
+ragged shapes; at B=2 H=32 N=8192 d=128 (bf16) a causal sliding window and a
+broadcast boolean mask on 256 sampled rows per head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_12_amd as fa
+import oracle
+from exact_attention_12_amd import inputs
+from gpu_util import TOL, errors, progress
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    progress("start " + request.node.nodeid)
+    yield
+
+
+def ext_inputs(cid, B, H, Hkv, Nq, Nk, d, dtype):
+    q = inputs.normal(1000 * cid + 0, (B, H, Nq, d), 1.0, dtype)
+    k = inputs.normal(1000 * cid + 1, (B, Hkv, Nk, d), 1.0, dtype)
+    v = inputs.normal(1000 * cid + 2, (B, Hkv, Nk, d), 1.0, dtype)
+    return q, k, v
+
+
+def check(q, k, v, causal, window, mask, dev, label, rows=None):
+    B, H, Nq, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    progress("fa_fwd_ext %s Nq=%d Nk=%d causal=%d window=%s mask=%s" % (
+        label, Nq, k.shape[2], causal, window, None if mask is None else tuple(mask.shape)))
+    o, lse = fa.forward_ext(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal,
+                            window=window, mask=None if mask is None else mask.to(dev))
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_ext(q, k, v, scale, causal, window, mask, rows=rows)
+    og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    if rows is not None:
+        og, lg = og[:, :, rows], lg[:, :, rows]
+    empty = np.isneginf(rl)
+    assert np.all(og[empty] == 0) and np.all(np.isneginf(lg[empty])), label
+    ok = ~empty
+    assert np.all(np.isfinite(og[ok])) and np.all(np.isfinite(lg[ok])), label
+    tol = TOL[q.dtype]
+    omax, omean = errors(og[ok], ro[ok])
+    lmax, _ = errors(lg[ok], rl[ok])
+    progress("%s rows=%d empty=%d max|dO|=%.3g mean|dO|=%.3g max|dlse|=%.3g" % (
+        label, ok.sum(), empty.sum(), omax, omean, lmax))
+    assert omax <= tol["o_max"] and omean <= tol["o_mean"] and lmax <= tol["lse_max"], (
+        label, omax, omean, lmax)
+
+
+WINDOWS = [  # Nq, Nk, causal, window
+    (100, 1000, True, (-1, -1)),    # chunked prefill: new rows at the end of a context
+    (333, 333, True, (-1, -1)),     # square: fa_fwd's causal mask
+    (300, 100, True, (-1, -1)),     # more queries than keys: the first 200 rows see nothing
+    (1000, 1000, True, (128, -1)),  # causal sliding window
+    (700, 700, False, (64, 64)),    # symmetric window
+    (257, 513, False, (0, 0)),      # one key per row
+    (190, 190, False, (-1, 30)),    # right window only
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("Nq,Nk,causal,window", WINDOWS)
+def test_windows(gpu, fa_lib, dt, Nq, Nk, causal, window):
+    d = 64 if dt == "f32" else 128
+    q, k, v = ext_inputs(60, 1, 4, 2, Nq, Nk, d, DT[dt])
+    check(q, k, v, causal, window, None, gpu, "%s %s" % (dt, window))
+
+
+MASKS = [  # mask shape prefix, Nq, Nk, causal, window, density
+    ((), 200, 301, False, (-1, -1), 0.5),   # broadcast, Nk not a multiple of 4
+    ((4,), 129, 256, False, (-1, -1), 0.3),  # per head
+    ((2, 1), 150, 150, True, (-1, -1), 0.7),  # per batch, with causal
+    ((2, 4), 64, 640, False, (100, 50), 0.9),  # per (b, h), with a window
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("prefix,Nq,Nk,causal,window,density", MASKS)
+def test_boolean_masks(gpu, fa_lib, dt, prefix, Nq, Nk, causal, window, density):
+    d = 128 if dt == "bf16" else 64
+    q, k, v = ext_inputs(61, 2, 4, 4, Nq, Nk, d, DT[dt])
+    g = np.random.default_rng(62 + Nq)
+    m = torch.from_numpy(g.random(prefix + (Nq, Nk)) < density)
+    m[..., 5, :] = False  # a row with no admissible key
+    if len(prefix) == 0:
+        m[:, 64:128] = False  # a fully masked key tile
+    check(q, k, v, causal, window, m, gpu, "%s mask%s" % (dt, prefix))
+
+
+def test_tril_mask_equals_causal(gpu, fa_lib):
+    """The pages' example: attn_mask = tril(ones) gives the causal result."""
+    q, k, v = ext_inputs(63, 1, 2, 2, 300, 300, 128, torch.bfloat16)
+    m = torch.ones(300, 300, dtype=torch.bool).tril()
+    dev = gpu
+    a = fa.forward_ext(q.to(dev), k.to(dev), v.to(dev), causal=False, mask=m.to(dev))
+    b = fa.forward(q.to(dev), k.to(dev), v.to(dev), causal=True)
+    torch.cuda.synchronize()
+    assert (a[0] - b[0]).abs().max().item() <= 1e-2 and (a[1] - b[1]).abs().max().item() <= 1e-3
+    check(q, k, v, False, (-1, -1), m, dev, "tril")
+
+
+def test_headline_sliding_window_sampled(gpu, fa_lib):
+    cfg = inputs.FWD_CONFIGS[3]
+    q, k, v = inputs.fwd_inputs(cfg)
+    rows = inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5)
+    check(q, k, v, True, (1024, -1), None, gpu, "B2 H32 N8192 window 1024", rows=rows)
+
+
+def test_headline_boolean_mask_sampled(gpu, fa_lib):
+    cfg = inputs.FWD_CONFIGS[3]
+    q, k, v = inputs.fwd_inputs(cfg)
+    N = cfg.N
+    # block-sparse causal pattern: each 64-key block is kept with probability 1/2
+    keep = torch.from_numpy(np.random.default_rng(64).random((N // 128, N // 64)) < 0.5)
+    m = keep.repeat_interleave(128, 0).repeat_interleave(64, 1) & torch.ones(N, N, dtype=torch.bool).tril()
+    m[:, 0] = True
+    rows = inputs.sample_rows(N, 256, seed=1000 * cfg.cid + 5)
+    check(q, k, v, False, (-1, -1), m, gpu, "B2 H32 N8192 block-sparse mask", rows=rows)

@@ -111,3 +111,12 @@ def test_all_true_mask_is_unmasked():
     a = oracle.attention_ext(q, k, v, 0.6, False, mask=torch.ones(9, 21, dtype=torch.bool))
     b = oracle.attention_ext(q, k, v, 0.6, False)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_sampled_rows_match_full():
+    q, k, v = rnd(21, (2, 2, 40, 8)), rnd(22, (2, 2, 70, 8)), rnd(23, (2, 2, 70, 8))
+    m = torch.from_numpy(np.random.default_rng(24).random((40, 70)) < 0.5)
+    full = oracle.attention_ext(q, k, v, 0.4, True, (9, -1), mask=m)
+    rows = [39, 0, 17]
+    part = oracle.attention_ext(q, k, v, 0.4, True, (9, -1), mask=m, rows=rows)
+    assert np.array_equal(part[0], full[0][:, :, rows]) and np.array_equal(part[1], full[1][:, :, rows])
