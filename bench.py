@@ -13,7 +13,10 @@ One step = one pass of the whole path over one batch of synthetic input:
   5. fa_bwd on the forward workload (bwd): dQ, dK, dV for a seeded N(0,1)
      upstream gradient, from step 1's o and lse;
   6. fa_fwd_fp8 on the forward workload quantised to block-scaled E4M3
-     (fwd_fp8), and fa_quant_fp8 of its q, k, v (quant_fp8).
+     (fwd_fp8), and fa_quant_fp8 of its q, k, v (quant_fp8);
+  7. fa_fwd_ext on the forward workload with a causal sliding window of 1024
+     keys (fwd_window) and with a block-sparse causal boolean mask
+     (fwd_mask: each (128-query, 64-key) block kept with probability 1/2).
 Inputs are generated on the host with fixed seeds and copied to HBM before
 the timed region.  The timed region runs K steps between two device
 synchronisations; each kernel call is bracketed by HIP events recorded on the
@@ -196,6 +199,19 @@ def main():
     o8 = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     lse8 = torch.empty((B, H, N), dtype=torch.float32, device=dev)
 
+    log("building the block-sparse mask")
+    win = 1024
+    keep = np.random.default_rng(64).random((N // 128, N // 64)) < 0.5
+    mask_h = np.repeat(np.repeat(keep, 128, 0), 64, 1) & np.tri(N, N, dtype=bool)
+    mask_h[:, 0] = True
+    mask_d = torch.from_numpy(mask_h.astype(np.uint8)).to(dev)
+    mask_pairs = int(mask_h.sum())
+    del mask_h
+    ow = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    lw = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    om = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    lm = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
     stream = torch.cuda.current_stream()
 
     def step(evs=None):
@@ -227,13 +243,20 @@ def main():
         fa.fa_quant_fp8(vd, B, H, N, d, 1, v8, ve8, stream=stream)
         if evs:
             evs[7].record(stream)
+        fa.fa_fwd_ext(qd, kd, vd, ow, lw, B, H, H, N, N, d, fscale, True, win, -1, stream=stream)
+        if evs:
+            evs[8].record(stream)
+        fa.fa_fwd_ext(qd, kd, vd, om, lm, B, H, H, N, N, d, fscale, True, -1, -1, mask_d, 0, 0,
+                      stream=stream)
+        if evs:
+            evs[9].record(stream)
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -264,11 +287,20 @@ def main():
     qz_bytes = 3 * nel * qd.element_size() + 2 * nel + fa.fa_fp8_codes_bytes(B, H, N, d, 1) \
         + 3 * B * H * ((N + 127) // 128) * 4
     qz_gbs = qz_bytes / (qz_avg * 1e-3) / 1e9
+    # flop over the visible (query, key) pairs only
+    win_pairs = sum(min(i + 1, win + 1) for i in range(N))
+    win_flops = 4.0 * B * H * d * win_pairs
+    mk_flops = 4.0 * B * H * d * mask_pairs
+    win_ms = [e[7].elapsed_time(e[8]) for e in evs]
+    mk_ms = [e[8].elapsed_time(e[9]) for e in evs]
+    win_avg, mk_avg = sum(win_ms) / len(win_ms), sum(mk_ms) / len(mk_ms)
+    win_tf = win_flops / (win_avg * 1e-3) / 1e12
+    mk_tf = mk_flops / (mk_avg * 1e-3) / 1e12
 
     # quick sanity of the last step's results (full parity lives in the tests)
     finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item()
                   and torch.isfinite(gout).all().item() and torch.isfinite(go).all().item()
-                  and all(torch.isfinite(t).all().item() for t in (bdq, bdk, bdv, o8)))
+                  and all(torch.isfinite(t).all().item() for t in (bdq, bdk, bdv, o8, ow, om)))
 
     flops = fcfg.flops()
     tflops = flops / (fwd_avg * 1e-3) / 1e12
@@ -366,6 +398,24 @@ def main():
                                    "frac": round(qz_gbs / PEAK_HBM_GBS, 4),
                                    "kernel": "fa_quant_fp8_kernel x3",
                                    "algorithmic_per_launch": qz_bytes}},
+        "fwd_window": {"metric": "attention forward TFLOP/s over visible pairs, causal sliding window",
+                       "value": round(win_tf, 2), "unit": "TFLOP/s",
+                       "workload": fcfg.name + ", window 1024 keys", "kernel_ms_avg": round(win_avg, 4),
+                       "roofline": {"bound": "mfma", "achieved": round(win_tf, 2),
+                                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": round(win_tf / PEAK_BF16_TFLOPS, 4),
+                                    "kernel": "fa_fwd_kernel<bf16,128,ext>",
+                                    "algorithmic_per_launch": win_flops}},
+        "fwd_mask": {"metric": "attention forward TFLOP/s over visible pairs, boolean mask",
+                     "value": round(mk_tf, 2), "unit": "TFLOP/s",
+                     "workload": fcfg.name + ", block-sparse causal uint8 mask (" +
+                                 "%.3f of the causal pairs)" % (mask_pairs / (N * (N + 1) / 2)),
+                     "kernel_ms_avg": round(mk_avg, 4),
+                     "roofline": {"bound": "mfma", "achieved": round(mk_tf, 2),
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(mk_tf / PEAK_BF16_TFLOPS, 4),
+                                  "kernel": "fa_fwd_kernel<bf16,128,ext+mask>",
+                                  "algorithmic_per_launch": mk_flops}},
         "decode_gqa": {"metric": "paged decode HBM bandwidth, 4 query heads per kv head",
                        "value": round(gqa_gbs, 1), "unit": "GB/s",
                        "workload": gcfg.name, "sum_ctx": int(gctx.sum()),

@@ -65,7 +65,8 @@ def load_library():
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_gqa.restype = i
     i64 = ctypes.c_int64
-    lib.fa_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, i64, i64, i, vp]
+    lib.fa_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, i64, i64, i64, i,
+                               vp]
     lib.fa_fwd_ext.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
@@ -144,15 +145,16 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype=None, stre
 
 
 def fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window_left=-1,
-               window_right=-1, mask=None, mask_stride_b=0, mask_stride_h=0, dtype=None,
-               stream=None):
+               window_right=-1, mask=None, mask_stride_b=0, mask_stride_h=0, mask_ld=None,
+               dtype=None, stream=None):
     """C entry point ``fa_fwd_ext``: rectangular / windowed / boolean-masked forward."""
     if dtype is None:
         dtype = _dtype_code(q.dtype)
     st = load_library().fa_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                    int(Hkv), int(Nq), int(Nk), int(d), float(scale),
                                    int(bool(causal)), int(window_left), int(window_right),
-                                   _ptr(mask), int(mask_stride_b), int(mask_stride_h), int(dtype),
+                                   _ptr(mask), int(mask_stride_b), int(mask_stride_h),
+                                   int(Nk if mask_ld is None else mask_ld), int(dtype),
                                    _stream(stream))
     if st != 0:
         raise FAError(st, "fa_fwd_ext")
@@ -285,14 +287,18 @@ def forward_ext(q, k, v, scale=None, causal=False, window=(-1, -1), mask=None, s
             m = m.unsqueeze(0)
         if m.shape[2:] != (Nq, Nk) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
             raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
-        mask = m.to(torch.uint8).contiguous()
-        sb = 0 if m.shape[0] == 1 else m.shape[1] * Nq * Nk
-        sh = 0 if m.shape[1] == 1 else Nq * Nk
+        # rows padded to a multiple of 16 bytes, as the kernel streams 16-byte chunks
+        ldm = (Nk + 15) // 16 * 16
+        padded = torch.zeros(m.shape[:3] + (ldm,), dtype=torch.uint8, device=m.device)
+        padded[..., :Nk] = m.to(torch.uint8)
+        mask = padded
+        sb = 0 if m.shape[0] == 1 else m.shape[1] * Nq * ldm
+        sh = 0 if m.shape[1] == 1 else Nq * ldm
         _check_dev("mask", mask, torch.uint8)
     o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window[0], window[1], mask,
-               sb, sh, stream=stream)
+               sb, sh, None if mask is None else mask.shape[-1], stream=stream)
     return o, lse
 
 

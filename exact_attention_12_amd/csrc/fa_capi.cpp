@@ -26,7 +26,7 @@ hipError_t bwd_dispatch(const void *q, const void *k, const void *v, const float
 size_t bwd_workspace_bytes(int B, int H, int N);
 hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
                             int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int wl,
-                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int dtype,
+                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int ldm, int dtype,
                             hipStream_t stream);
 hipError_t quant_fp8_dispatch(const void *x, int dtype, int B, int H, int N, int d, int layout,
                               void *codes, int32_t *exps, hipStream_t stream);
@@ -115,27 +115,30 @@ extern "C" int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o,
 extern "C" int fa_fwd_ext(const void *q, const void *k, const void *v, float *o, float *lse, int B,
                           int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                           int window_left, int window_right, const uint8_t *mask,
-                          int64_t mask_stride_b, int64_t mask_stride_h, int dtype, void *stream)
+                          int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_ld, int dtype,
+                          void *stream)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
     if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
-    if (mask && (mask_stride_b < 0 || mask_stride_h < 0)) return FA_ERR_INVALID_ARG;
+    if (mask && (mask_stride_b < 0 || mask_stride_h < 0 || mask_ld < Nk)) return FA_ERR_INVALID_ARG;
     const int es = elem_bytes(dtype);
     if (es == 0) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     const int64_t qtiles = ((int64_t)Nq + kFwdRowsPerWorkgroup - 1) / kFwdRowsPerWorkgroup;
     if ((int64_t)B * H * qtiles > INT_MAX) return FA_ERR_UNSUPPORTED;
     if ((int64_t)Nk * d * es > INT_MAX || (int64_t)Nq + Nk > INT_MAX / 4) return FA_ERR_UNSUPPORTED;
-    if (mask && (int64_t)Nq * Nk > INT_MAX) return FA_ERR_UNSUPPORTED;  // one mask slice < 2 GiB
+    if (mask && (int64_t)Nq * mask_ld > INT_MAX) return FA_ERR_UNSUPPORTED;  // one mask slice < 2 GiB
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(lse, 4))
+        return FA_ERR_ALIGNMENT;
+    if (mask && (!aligned(mask, 16) || mask_ld % 16 || mask_stride_b % 16 || mask_stride_h % 16))
         return FA_ERR_ALIGNMENT;
     const uint64_t rows = (uint64_t)B * H * Nq, kv_rows = (uint64_t)B * Hkv * Nk;
     const uint64_t o_bytes = rows * d * 4, l_bytes = rows * 4;
     const uint64_t m_bytes =
-        mask ? (uint64_t)(B - 1) * mask_stride_b + (uint64_t)(H - 1) * mask_stride_h + (uint64_t)Nq * Nk : 0;
+        mask ? (uint64_t)(B - 1) * mask_stride_b + (uint64_t)(H - 1) * mask_stride_h + (uint64_t)Nq * mask_ld : 0;
     if (overlap(o, o_bytes, lse, l_bytes)) return FA_ERR_INVALID_ARG;
     const void *ins[4] = {q, k, v, mask};
     const uint64_t in_bytes[4] = {rows * d * es, kv_rows * d * es, kv_rows * d * es, m_bytes};
@@ -144,7 +147,8 @@ extern "C" int fa_fwd_ext(const void *q, const void *k, const void *v, float *o,
             return FA_ERR_INVALID_ARG;
     const hipError_t e =
         fa::fwd_ext_dispatch(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, window_left,
-                             window_right, mask, mask_stride_b, mask_stride_h, dtype, (hipStream_t)stream);
+                             window_right, mask, mask_stride_b, mask_stride_h, (int)mask_ld, dtype,
+                             (hipStream_t)stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

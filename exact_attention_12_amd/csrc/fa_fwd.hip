@@ -76,8 +76,9 @@ constexpr float kPMax = 16384.0f;
 struct FwdExt {
     int Nk;               // keys (the kernel's N counts query rows)
     int off, wl, wr;      // diagonal offset and window, all pre-clamped by the host
-    const uint8_t *mask;  // uint8 [.., Nq, Nk] or null
-    int64_t msb, msh;     // element strides of the mask between batches and heads
+    const uint8_t *mask;  // uint8 [.., Nq, ldm] or null
+    int64_t msb, msh;     // byte strides of the mask between batches and heads
+    int ldm;              // byte stride between mask rows (a multiple of 16, >= Nk)
 };
 
 // EXT: 0 = square path (N queries and keys, optional top-left causal mask),
@@ -96,7 +97,14 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int KW = C::KW;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
+    // boolean mask: a (BR x BC)-byte tile of it rides along with each K/V tile,
+    // rows of BC bytes with the 16-byte chunks swizzled by swzm()
+    constexpr int MCPR = C::BC / 16;                            // 16-byte chunks per mask row
+    constexpr int MASKB = EXT == 2 ? C::BR * C::BC : 0;         // mask tile bytes
+    constexpr int NLDM_W = EXT == 2 ? C::BR * MCPR / kWave / 4 : 0;  // its 1 KiB loads per wave
+    constexpr int SB = C::STAGEB + MASKB;                        // bytes per stage
+    auto swzm = [](int row) { return MCPR == 4 ? (row >> 2) & 3 : (row >> 3) & 1; };
+    __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -150,9 +158,25 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     const int head_bytes = NK * C::ROWB;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)Kh, 0, head_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)Vh, 0, head_bytes, kBufferFlags);
+    const uint8_t *mbase = nullptr;
+    if constexpr (EXT == 2) mbase = ext.mask + (int64_t)(bh / H) * ext.msb + (int64_t)(bh % H) * ext.msh;
+    const __amdgpu_buffer_rsrc_t mrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)mbase, 0, EXT == 2 ? N * ext.ldm : 0, kBufferFlags);
+    // per-lane mask-tile load offsets (set per query tile): load I, lane l
+    // fills chunk position p = I*64 + l = row p / MCPR, position p % MCPR
+    // holding chunk (p % MCPR) ^ swzm(row) of mask row q0 + row
+    int m_off[NLDM_W > 0 ? NLDM_W : 1];
+    auto set_mask_offsets = [&](int q0_) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NLDM_W; ++i) {
+            const int p = (wave * NLDM_W + i) * kWave + lane;
+            const int row = p / MCPR;
+            m_off[i] = (q0_ + row) * ext.ldm + ((p % MCPR) ^ swzm(row)) * 16;
+        }
+    };
     auto load_tile = [&](int j, int buf) {
         const int k0 = j * C::BC;
-        char *kd = smem + buf * C::STAGEB;
+        char *kd = smem + buf * SB;
         char *vd = kd + C::TILEB;
         const int soff = k0 * C::ROWB;
         if (k0 + C::BC <= NK) {
@@ -172,6 +196,12 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                 buffer_load_lds16(krs, kd + I * 1024, off, soff);
                 buffer_load_lds16(vrs, vd + I * 1024, off, soff);
             }
+        }
+        if constexpr (EXT == 2) {
+            // rows past the end of the mask read as 0 (buffer bounds)
+#pragma unroll
+            for (int i = 0; i < NLDM_W; ++i)
+                buffer_load_lds16(mrs, kd + C::STAGEB + (wave * NLDM_W + i) * 1024, m_off[i], k0);
         }
     };
     // byte offset of element e of row r in a swizzled tile
@@ -209,7 +239,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // K operands are read from LDS in groups of two steps, one group
     // ahead of the matrix products that use them.
     auto qk = [&](const char *Ks, f32x16 (&s)[C::NKB]) {
-        constexpr int G = 2;
+        constexpr int G = EXT == 2 ? 1 : 2;  // registers for the boolean mask
         constexpr int NG = C::QK_STEPS / G;
         frag kf[2][G][C::NKB];
         auto rd = [&](int g, int b) {
@@ -252,39 +282,22 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             lo[kb] = first - k0 - kb * 32 - 4 * h;
         }
     };
-    // mask bytes of keys k0 + kb*32 + 8g + 4h + 0..3, one dword per (kb, g);
-    // reads past the mask (ragged tail) return 0 = masked
-    const uint8_t *mbase = nullptr;
-    if constexpr (EXT == 2) mbase = ext.mask + (int64_t)(bh / H) * ext.msb + (int64_t)(bh % H) * ext.msh;
-    const __amdgpu_buffer_rsrc_t mrs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)mbase, 0, EXT == 2 ? N * NK : 0, kBufferFlags);
-    int mrow = 0;
-    auto load_mask = [&](int k0, uint32_t (&mw)[C::NKB][4]) __attribute__((always_inline)) {
-        if constexpr (EXT == 2) {
-            const int base = mrow + k0 + 4 * h;
-            if ((NK & 3) == 0) {
+    // mask bytes of keys k0 + kb*32 + 8g + 4h + 0..3 of this lane's row, one
+    // dword per (kb, g), from the tile's mask in LDS
+    auto read_mask = [&](const char *Ms, uint32_t (&mw)[C::NKB][4]) __attribute__((always_inline)) {
+        const int row = wave * 32 + col;
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
+        for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        mw[kb][g] = __builtin_amdgcn_raw_buffer_load_b32(mrs, base + kb * 32 + 8 * g, 0, 0);
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        uint32_t w = 0;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(mrs, base + kb * 32 + 8 * g + e, 0, 0)
-                                 << (8 * e);
-                        mw[kb][g] = w;
-                    }
+            for (int g = 0; g < 4; ++g) {
+                const int chunk = 2 * kb + g / 2;
+                mw[kb][g] = *(const uint32_t *)(Ms + row * C::BC + ((chunk ^ swzm(row)) * 16) + 8 * (g % 2) + 4 * h);
             }
-        }
     };
+    // returns the visible scores as bits kb*16 + r (used by the boolean mask)
     auto apply_mask = [&](f32x16 (&s)[C::NKB], const int (&lim)[C::NKB], const int (&lo)[C::NKB],
                           const uint32_t (&mw)[C::NKB][4]) {
+        uint32_t bits = 0;
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -293,10 +306,20 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                 if constexpr (EXT != 0) off_ = off_ || acc_row(r, 0) < lo[kb];
                 if constexpr (EXT == 2) off_ = off_ || ((mw[kb][r / 4] >> (8 * (r % 4))) & 0xffu) == 0;
                 if (off_) s[kb][r] = -INFINITY;
+                else bits |= 1u << (kb * 16 + r);
             }
+        return bits;
+    };
+    auto apply_bits = [&](f32x16 (&s)[C::NKB], uint32_t bits) {
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (!((bits >> (kb * 16 + r)) & 1u)) s[kb][r] = -INFINITY;
     };
     // first and last key tiles of this wave's rows (general masks)
     int jw_beg = 0, jw_end = 0;
+
     // Move the reference to the row max of this tile where that is larger,
     // rescaling what was accumulated against the old reference.
     auto rebase = [&](const f32x16 (&s)[C::NKB]) {
@@ -335,19 +358,28 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // One K/V tile: j is the tile, STAGE (= j % 2) its LDS buffer.
     auto tile = [&](int j, auto stage_c) {
         constexpr int STAGE = decltype(stage_c)::value;
-        if (j + 1 < ntiles) load_tile(j + 1, STAGE ^ 1);
         const int k0 = j * C::BC;
-        const char *Ks = smem + STAGE * C::STAGEB;
+        if (j + 1 < ntiles) load_tile(j + 1, STAGE ^ 1);
+        uint32_t mcur[C::NKB][4];
+        if constexpr (EXT == 2) read_mask(smem + STAGE * SB + C::STAGEB, mcur);
+        const char *Ks = smem + STAGE * SB;
         const char *Vs = Ks + C::TILEB;
 
-        if (EXT != 0 && (j < jw_beg || j >= jw_end)) {
-            // no row of this wave sees a key of this tile
+        bool skip = EXT != 0 && (j < jw_beg || j >= jw_end);  // no row of the wave sees a key here
+        if constexpr (EXT == 2) {
+            // ... or the mask hides every key of the tile from every row of the wave
+            uint32_t any = 0;
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) any |= mcur[kb][g];
+            skip = skip || __builtin_amdgcn_ballot_w64(any != 0) == 0;
+        }
+        if (skip) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             return;
         }
-        uint32_t mw[C::NKB][4];
-        load_mask(k0, mw);
         f32x16 s[C::NKB];
         qk(Ks, s);
         bool need_mask = (k0 + C::BC > NK) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
@@ -357,7 +389,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         if constexpr (EXT == 2) need_mask = true;
         int lim[C::NKB], lo[C::NKB];
         limits(k0, lim, lo);
-        if (need_mask) apply_mask(s, lim, lo, mw);
+        uint32_t vis = 0;
+        if (need_mask) vis = apply_mask(s, lim, lo, mcur);
 
         // Lazy reference max.  The probabilities are taken relative to a
         // reference m_ref instead of the running max: exp(s - m) =
@@ -374,7 +407,10 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         float rs = exponentiate(s);
         if ((EXT != 0 || j != 0) && __builtin_amdgcn_ballot_w64(!(rs <= kPMax)) != 0) {
             qk(Ks, s);
-            if (need_mask) apply_mask(s, lim, lo, mw);
+            if (need_mask) {
+                if constexpr (EXT == 2) apply_bits(s, vis);
+                else apply_mask(s, lim, lo, mcur);
+            }
             rebase(s);
             rs = exponentiate(s);
         }
@@ -426,7 +462,9 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     };
 
   for (int item = 0; item < (CAUSAL ? 2 : 1); ++item) {
-    const int qt = CAUSAL ? (item == 0 ? num_qtiles - 1 - pi : pi) : pi;
+    // General masks: the last query tiles see the most keys when the diagonal
+    // is aligned bottom-right; dispatch them first so the grid drains evenly.
+    const int qt = CAUSAL ? (item == 0 ? num_qtiles - 1 - pi : pi) : (EXT != 0 ? num_qtiles - 1 - pi : pi);
     if (CAUSAL && item == 1 && qt == num_qtiles - 1 - pi) break;  // odd count: middle tile alone
     q0 = qt * C::BR;
     qrow = q0 + wave * 32 + col;
@@ -454,7 +492,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         const int kw_end = min(NK, w_last + ext.off + ext.wr + 1);
         jw_beg = kw_beg / C::BC;
         jw_end = (wq_lo < N && kw_end > kw_beg) ? (kw_end + C::BC - 1) / C::BC : 0;
-        mrow = min(qrow, N - 1) * NK;
+        if constexpr (EXT == 2) set_mask_offsets(q0);
     }
     ntiles = kend > jbeg * C::BC ? (kend + C::BC - 1) / C::BC : jbeg;
 #pragma unroll
@@ -522,7 +560,7 @@ static hipError_t launch_fwd(const void *q, const void *k, const void *v, float 
     const int64_t grid = (int64_t)B * H * (CAUSAL ? (nqt + 1) / 2 : nqt);
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 0>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, o, lse, N, nqt, scale, H, H / Hkv,
-                       FwdExt{N, 0, 0, 0, nullptr, 0, 0});
+                       FwdExt{N, 0, 0, 0, nullptr, 0, 0, 0});
     return hipGetLastError();
 }
 
@@ -577,7 +615,7 @@ hipError_t fwd_dispatch(const void *q, const void *k, const void *v, float *o, f
 // the window bounds (< 0 = unbounded); causal limits the right bound to 0.
 hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
                             int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int wl,
-                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int dtype,
+                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int ldm, int dtype,
                             hipStream_t stream)
 {
     // bounds beyond Nq + Nk are unbounded; keep every sum inside int
@@ -585,7 +623,7 @@ hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *
     int r = wr < 0 ? big : min(wr, big);
     if (causal) r = min(r, 0);
     const int l = wl < 0 ? big : min(wl, big);
-    const FwdExt ext{Nk, Nk - Nq, l, r, mask, msb, msh};
+    const FwdExt ext{Nk, Nk - Nq, l, r, mask, msb, msh, ldm};
     switch (dtype) {
     case 0:
         return d == 64 ? launch_fwd_ext<float, 64>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream)

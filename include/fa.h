@@ -125,13 +125,16 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse
  *       and (window_left < 0 or j >= i + off - window_left)
  *       and (window_right < 0 or j <= i + off + window_right)
  *       and (mask == NULL or mask[b * mask_stride_b + h * mask_stride_h
- *                                 + i * Nk + j] != 0),
+ *                                 + i * mask_ld + j] != 0),
  *   with off = Nk - Nq: the last query row is aligned with the last key (new
  *   tokens appended to a context).  Nq = Nk, causal, no window and no mask
  *   is fa_fwd's causal mask.
- *   mask      : uint8 (0 = masked), rows of Nk bytes per (b, h) slice at the
- *               given element strides (0 broadcasts over that dimension), or
- *               NULL.  Nq * Nk must stay below 2^31.
+ *   mask      : uint8 (0 = masked), or NULL: the (b, h) slice starts at byte
+ *               b * mask_stride_b + h * mask_stride_h (0 broadcasts over that
+ *               dimension) and holds Nq rows mask_ld bytes apart, of which
+ *               the first Nk are used.  mask, mask_ld and both strides must
+ *               be multiples of 16 (else FA_ERR_ALIGNMENT; pad the rows),
+ *               mask_ld >= Nk, and Nq * mask_ld below 2^31.
  *   A row that sees no key gets o = 0 and lse = -inf.
  * Every other argument and the error behaviour are those of fa_fwd_gqa; o
  * and lse must not overlap q, k, v or the mask.
@@ -139,7 +142,7 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse
 int fa_fwd_ext(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
                int Hkv, int Nq, int Nk, int d, float scale, int causal, int window_left,
                int window_right, const uint8_t *mask, int64_t mask_stride_b, int64_t mask_stride_h,
-               int dtype, void *stream);
+               int64_t mask_ld, int dtype, void *stream);
 
 /*
  * fa_bwd_workspace_size -- bytes of device workspace that fa_bwd needs: two

@@ -150,9 +150,9 @@ def test_bwd_workspace_size(fa_lib):
 
 
 def fext(lib, q=P, k=P, v=P, o=FAR[0], lse=FAR[1], B=1, H=2, Hkv=1, Nq=10, Nk=30, d=64,
-         scale=0.125, causal=1, wl=-1, wr=-1, mask=None, sb=0, sh=0, dtype=1):
+         scale=0.125, causal=1, wl=-1, wr=-1, mask=None, sb=0, sh=0, ldm=32, dtype=1):
     return lib.fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, wl, wr, mask, sb, sh,
-                          dtype, None)
+                          ldm, dtype, None)
 
 
 def test_fwd_ext_validation(fa_lib):
@@ -163,7 +163,11 @@ def test_fwd_ext_validation(fa_lib):
     assert fext(fa_lib, mask=FAR[2], sb=-1) == INVALID
     assert fext(fa_lib, dtype=4) == INVALID
     assert fext(fa_lib, d=80) == UNSUPPORTED
-    assert fext(fa_lib, mask=FAR[2], Nq=1 << 16, Nk=1 << 16) == UNSUPPORTED  # mask slice >= 2^31
+    assert fext(fa_lib, mask=FAR[2], Nq=1 << 16, Nk=1 << 16, ldm=1 << 16) == UNSUPPORTED  # slice >= 2^31
+    assert fext(fa_lib, mask=FAR[2], ldm=16) == INVALID           # row stride below Nk
+    assert fext(fa_lib, mask=FAR[2], ldm=40) == ALIGN             # row stride not a multiple of 16
+    assert fext(fa_lib, mask=FAR[2] + 8) == ALIGN
+    assert fext(fa_lib, mask=FAR[2], sh=8) == ALIGN
     assert fext(fa_lib, k=P + 4) == ALIGN
     assert fext(fa_lib, o=P) == INVALID                 # o overlaps q
     assert fext(fa_lib, o=FAR[2], mask=FAR[2] + 64) == INVALID  # o overlaps the mask
