@@ -8,6 +8,7 @@ suites (tests/test_oracle_pins.py, test_oracle_decode.py,
 test_oracle_tiling.py) against it in a subprocess.  The mutation passes only
 if at least one pin fails.  A control run of the unmodified copy must pass.
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -133,25 +134,40 @@ MUTATIONS = [
 ]
 
 
-def run_pins(tmp_path, source_text):
-    d = tmp_path / "oracle_copy"
-    d.mkdir(exist_ok=True)
-    src = d / "oracle.c"
-    src.write_text(source_text)
-    env = dict(os.environ, ORACLE_TEST_SOURCE=str(src), PYTHONDONTWRITEBYTECODE="1")
+def run_pins(workdir, source_text):
+    os.makedirs(workdir, exist_ok=True)
+    src = os.path.join(workdir, "oracle.c")
+    with open(src, "w") as f:
+        f.write(source_text)
+    env = dict(os.environ, ORACLE_TEST_SOURCE=src, PYTHONDONTWRITEBYTECODE="1")
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu"] + PIN_SUITES
-    return subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
 
 
-def test_control_copy_passes(tmp_path):
-    res = run_pins(tmp_path, open(SRC).read())
+@pytest.fixture(scope="module")
+def pin_runs(tmp_path_factory):
+    """Run the pin suites on the unmodified copy and on every mutated copy,
+    several subprocesses at a time; results by case name."""
+    text = open(SRC).read()
+    cases = {"control": text}
+    for name, old, new in MUTATIONS:
+        cases[name] = text.replace(old, new, 1) if text.count(old) >= 1 else None
+    base = tmp_path_factory.mktemp("oracle_mutations")
+    workers = max(1, min(8, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
+    results = {n: None for n in cases}  # None: the mutation site was not found
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+        futs = {n: pool.submit(run_pins, str(base / n), t) for n, t in cases.items() if t is not None}
+        results.update({n: f.result() for n, f in futs.items()})
+    return results
+
+
+def test_control_copy_passes(pin_runs):
+    res = pin_runs["control"]
     assert res.returncode == 0, res.stdout[-3000:] + res.stderr[-3000:]
 
 
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_mutation_is_caught(tmp_path, name, old, new):
-    text = open(SRC).read()
-    assert text.count(old) >= 1, "mutation site not found: " + name
-    mutated = text.replace(old, new, 1)
-    res = run_pins(tmp_path, mutated)
+def test_mutation_is_caught(pin_runs, name, old, new):
+    res = pin_runs[name]
+    assert res is not None, "mutation site not found: " + name
     assert res.returncode != 0, "no pin failed for mutation %s:\n%s" % (name, res.stdout[-2000:])
