@@ -322,6 +322,7 @@ def main():
     fwd_traffic = measured_traffic("fa_fwd_kernel", fwd_hash)
     dec_traffic = measured_traffic("fa_decode_partition_kernel", dec_hash)
     bwd_traffic = measured_traffic("fa_bwd", bwd_hash)
+    f8_traffic = measured_traffic("fa_fwd_fp8_kernel", source_hash("fa_fp8.hip", "fa_device.h", "fa_tile.h"))
 
     result = {
         "metric": "attn fwd TFLOP/s + % bf16 MFMA peak (N=8192,d=128,causal); decode HBM GB/s",
@@ -389,6 +390,7 @@ def main():
                     "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 2),
                                  "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4),
+                                 "traffic": f8_traffic,
                                  "kernel": "fa_fwd_fp8_kernel<causal>",
                                  "algorithmic_per_launch": fcfg.flops()}},
         "quant_fp8": {"metric": "block-scaled E4M3 quantisation of q, k, v (HBM GB/s)",
