@@ -32,6 +32,11 @@ constexpr int kDecBlk = kDecPart / kDecBS;  // cache blocks per partition (16)
 constexpr int kDecThreads = 256;  // 4 waves
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kDecBPW = kDecBlk / kDecWaves;  // blocks per wave (4)
+// Dynamic LDS the partition launch reserves (unused) so that at most two
+// workgroups share a compute unit's 160 KiB: a third one, which the register
+// count would allow, adds concurrent streams of scattered 4 KiB blocks and
+// measured about 2 % slower on the 64 x 32-head workload.
+constexpr int kDecLdsReserve = 56 * 1024;
 
 template <typename T> __device__ __forceinline__ float elem_to_f32(uint32_t bits16);
 template <> __device__ __forceinline__ float elem_to_f32<_Float16>(uint32_t b)
@@ -50,6 +55,46 @@ template <typename T> __device__ __forceinline__ float vec_elem(const u32x4 &v, 
     return elem_to_f32<T>((v[e / 2] >> (16 * (e % 2))) & 0xffffu);
 }
 
+// c + a.lo * b.lo + a.hi * b.hi for two packed 16-bit pairs, accumulated in
+// fp32 by the hardware's two-element dot instruction (the products of two
+// 16-bit values are exact in fp32).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);
+template <> __device__ __forceinline__ float dot2<_Float16>(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+template <> __device__ __forceinline__ float dot2<__bf16>(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                           false);
+}
+
+// q . k over the 8 head elements of one 16-byte vector pair
+template <typename T> __device__ __forceinline__ float dot8(const u32x4 &a, const u32x4 &b, float c)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = dot2<T>(a[e], b[e], c);
+    return c;
+}
+
+// Cache block ids of the blocks a wave handles (b = wave + kDecWaves * i of
+// the partition), read together with the context length rather than after
+// it: the index is clamped to the sequence's table row (which holds at
+// least one entry whenever a partition kernel runs), and entries past the
+// context are never used.
+template <int NB>
+__device__ __forceinline__ void load_block_ids(int (&blk)[NB], const int32_t *__restrict__ row, int first,
+                                               int stride, int max_blocks_per_seq)
+{
+#pragma unroll
+    for (int i = 0; i < NB; ++i) blk[i] = row[min(first + stride * i, max_blocks_per_seq - 1)];
+    // empty uses keep the loads above the caller's early exit
+#pragma unroll
+    for (int i = 0; i < NB; ++i) asm volatile("" : "+s"(blk[i]));
+}
+
 struct DecWs {
     float *o;  // [S, H, P, D]
     float *m;  // [S, H, P]
@@ -65,34 +110,30 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
                                 float scale, DecWs ws)
 {
     const int h = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int ctx = context_lens[s];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int t0 = p * kDecPart;
+    const int ctx = context_lens[s];
+    int blk[kDecBPW];
+    load_block_ids(blk, block_tables + (int64_t)s * max_blocks_per_seq, t0 / kDecBS + wave, kDecWaves,
+                   max_blocks_per_seq);
     const int64_t pidx = ((int64_t)s * num_heads + h) * nparts + p;
     if (t0 >= ctx) return;  // empty partition: the merge reads only partitions below ctx
     const int ntok = min(kDecPart, ctx - t0);
     const int nblk = (ntok + kDecBS - 1) / kDecBS;
     const int kvh = h / (num_heads / num_kv_heads);
 
-    __shared__ int tbl[kDecBlk];
     __shared__ __attribute__((aligned(16))) float logits[kDecPart];
     __shared__ float red[2][kDecWaves];
     __shared__ float part[kDecWaves][kDecD];
 
-    if (tid < nblk) tbl[tid] = block_tables[(int64_t)s * max_blocks_per_seq + t0 / kDecBS + tid];
-
-    // q elements this lane dots with: head groups g = lane/16 + 4c.
-    float qv[4][8];
+    // q elements this lane dots with, packed: head groups g = lane/16 + 4c.
+    u32x4 qv[4];
     {
         const T *qp = q + ((int64_t)s * num_heads + h) * kDecD;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 v = *(const u32x4 *)(qp + (lane / 16 + 4 * c) * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[c][e] = vec_elem<T>(v, e);
-        }
+        for (int c = 0; c < 4; ++c) qv[c] = *(const u32x4 *)(qp + (lane / 16 + 4 * c) * 8);
     }
-    __syncthreads();
 
     // Issue every K and V load of this wave's blocks up front.
     u32x4 kr[kDecBPW][4], vr[kDecBPW][4];
@@ -100,7 +141,7 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
     for (int i = 0; i < kDecBPW; ++i) {
         const int b = wave + kDecWaves * i;
         if (b < nblk) {
-            const int64_t base = ((int64_t)tbl[b] * num_kv_heads + kvh) * (kDecD * kDecBS);
+            const int64_t base = ((int64_t)blk[i] * num_kv_heads + kvh) * (kDecD * kDecBS);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 kr[i][c] = *(const u32x4 *)(kc + base + (lane + 64 * c) * 8);
@@ -117,9 +158,7 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
         if (b < nblk) {
             float dot = 0.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[c][e], vec_elem<T>(kr[i][c], e), dot);
+            for (int c = 0; c < 4; ++c) dot = dot8<T>(qv[c], kr[i][c], dot);
             dot += __shfl_xor(dot, 16, kWave);
             dot += __shfl_xor(dot, 32, kWave);
             const int tok = t0 + b * kDecBS + lane % 16;
@@ -198,7 +237,7 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
 // (kv head, sequence, partition) serves up to GM query heads of the group,
 // so each K/V block is read from HBM once per kv head instead of once per
 // query head.  The lane maps and the per-head softmax are those of the
-// kernel above; the queries sit in LDS (fp32) instead of registers, and every
+// kernel above; the queries sit in LDS (16-bit) instead of registers, and every
 // head has its own logits row, reductions and partial.
 template <typename T, int GM>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
@@ -213,34 +252,30 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
     const int kvh = blockIdx.x / ngroups, g0 = (blockIdx.x % ngroups) * GM;
     const int ng = min(GM, G - g0);  // query heads of this workgroup: kvh*G + g0 + g, g < ng
     const int s = blockIdx.y, p = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int ctx = context_lens[s];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int t0 = p * kDecPart;
+    const int ctx = context_lens[s];
+    int blk[kDecBPW];
+    load_block_ids(blk, block_tables + (int64_t)s * max_blocks_per_seq, t0 / kDecBS + wave, kDecWaves,
+                   max_blocks_per_seq);
     if (t0 >= ctx) return;  // empty partition: the merge reads only partitions below ctx
     const int ntok = min(kDecPart, ctx - t0);
     const int nblk = (ntok + kDecBS - 1) / kDecBS;
     const int h0 = kvh * G + g0;
 
-    __shared__ int tbl[kDecBlk];
-    __shared__ __attribute__((aligned(16))) float qs[GM][kDecD];
+    // the group's queries, kept in their 16-bit type (64 words per head)
+    __shared__ __attribute__((aligned(16))) uint32_t qs[GM][kDecD / 2];
     __shared__ __attribute__((aligned(16))) float logits[GM][kDecPart];
     __shared__ float red[2][GM][kDecWaves];
     __shared__ float part[kDecWaves][GM][kDecD];
-
-    if (tid < nblk) tbl[tid] = block_tables[(int64_t)s * max_blocks_per_seq + t0 / kDecBS + tid];
-    for (int i = tid; i < ng * kDecD; i += kDecThreads) {
-        const int g = i / kDecD, e = i % kDecD;
-        const T *qp = q + ((int64_t)s * num_heads + h0 + g) * kDecD;
-        qs[g][e] = (float)qp[e];
-    }
-    __syncthreads();
 
     u32x4 kr[kDecBPW][4], vr[kDecBPW][4];
 #pragma unroll
     for (int i = 0; i < kDecBPW; ++i) {
         const int b = wave + kDecWaves * i;
         if (b < nblk) {
-            const int64_t base = ((int64_t)tbl[b] * num_kv_heads + kvh) * (kDecD * kDecBS);
+            const int64_t base = ((int64_t)blk[i] * num_kv_heads + kvh) * (kDecD * kDecBS);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 kr[i][c] = *(const u32x4 *)(kc + base + (lane + 64 * c) * 8);
@@ -248,6 +283,11 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
             }
         }
     }
+    for (int i = tid; i < ng * (kDecD / 2); i += kDecThreads) {
+        const int g = i / (kDecD / 2), w = i % (kDecD / 2);
+        qs[g][w] = ((const uint32_t *)(q + ((int64_t)s * num_heads + h0 + g) * kDecD))[w];
+    }
+    __syncthreads();
 
     // logits per head: lane l dots token l % 16 with head groups l/16 + 4c
     float wmax[GM];
@@ -257,26 +297,14 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
     for (int i = 0; i < kDecBPW; ++i) {
         const int b = wave + kDecWaves * i;
         if (b < nblk) {
-            float kf[4][8];
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kf[c][e] = vec_elem<T>(kr[i][c], e);
             const int tok = t0 + b * kDecBS + lane % 16;
 #pragma unroll
             for (int g = 0; g < GM; ++g) {
                 if (g < ng) {
                     float dot = 0.f;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const f32x4 qa = *(const f32x4 *)(&qs[g][(lane / 16 + 4 * c) * 8]);
-                        const f32x4 qb = *(const f32x4 *)(&qs[g][(lane / 16 + 4 * c) * 8 + 4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            dot = __builtin_fmaf(qa[e], kf[c][e], dot);
-                            dot = __builtin_fmaf(qb[e], kf[c][e + 4], dot);
-                        }
-                    }
+                    for (int c = 0; c < 4; ++c)
+                        dot = dot8<T>(*(const u32x4 *)(&qs[g][(lane / 16 + 4 * c) * 4]), kr[i][c], dot);
                     dot += __shfl_xor(dot, 16, kWave);
                     dot += __shfl_xor(dot, 32, kWave);
                     const float lg = (tok < ctx) ? scale * dot : -INFINITY;
@@ -381,11 +409,12 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
 template <typename T> __device__ __forceinline__ T f32_to_elem(float x) { return (T)x; }
 
 // Merge of the partitions of one (sequence, head) row per wave, four rows
-// per workgroup.  Lanes first combine the partitions' maxima and weights
-// (partition p on lane p % 64), then every lane accumulates two head
-// elements over all partitions, the weight of partition p taken from lane
-// p % 64 of the chunk.
+// per workgroup, in chunks of kMergeChunk partitions: every load of a chunk
+// (maxima and sums on lanes 0..15, two head elements of each partial on
+// every lane) is issued at once, and the chunks combine with Eq. (4) of
+// "Flash Attention", the running result rescaled by e^(M_old - M_new).
 constexpr int kMergeRows = 4;
+constexpr int kMergeChunk = 16;
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_decode_merge_kernel(const int32_t *__restrict__ context_lens, T *__restrict__ out,
@@ -397,35 +426,35 @@ void fa_decode_merge_kernel(const int32_t *__restrict__ context_lens, T *__restr
     const int ctx = context_lens[r / num_heads];
     const int np = min(nparts, (ctx + kDecPart - 1) / kDecPart);
     const int64_t base = (int64_t)r * nparts;
-    float m = -INFINITY;
-    for (int p = lane; p < np; p += kWave) m = fmaxf(m, ws.m[base + p]);
-#pragma unroll
-    for (int off = 32; off >= 1; off /= 2) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    float wsum = 0.f;
-    float o0 = 0.f, o1 = 0.f;
-    for (int p0 = 0; p0 < np; p0 += kWave) {
-        const int p = p0 + lane;
-        const float w = (p < np) ? ws.l[base + p] * exp2_hw((ws.m[base + p] - m) * kLog2e) : 0.f;
-        wsum += w;
-        const int n = min(kWave, np - p0);
-        int i = 0;
-        for (; i + 8 <= n; i += 8) {
-            f32x2 ov[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) ov[k] = *(const f32x2 *)(ws.o + (base + p0 + i + k) * kDecD + 2 * lane);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float wk = __shfl(w, i + k, kWave);
-                o0 = __builtin_fmaf(wk, ov[k][0], o0);
-                o1 = __builtin_fmaf(wk, ov[k][1], o1);
-            }
+    float M = -INFINITY, wsum = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int p0 = 0; p0 < np; p0 += kMergeChunk) {
+        const int n = min(kMergeChunk, np - p0);
+        float mj = -INFINITY, lj = 0.f;
+        if (lane < n) {
+            mj = ws.m[base + p0 + lane];
+            lj = ws.l[base + p0 + lane];
         }
-        for (; i < n; ++i) {
-            const f32x2 ov = *(const f32x2 *)(ws.o + (base + p0 + i) * kDecD + 2 * lane);
-            const float wk = __shfl(w, i, kWave);
-            o0 = __builtin_fmaf(wk, ov[0], o0);
-            o1 = __builtin_fmaf(wk, ov[1], o1);
+        f32x2 ov[kMergeChunk];
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k)
+            ov[k] = k < n ? *(const f32x2 *)(ws.o + (base + p0 + k) * kDecD + 2 * lane) : f32x2{0.f, 0.f};
+        // every partition below np holds at least one token, so mc is finite
+        float mc = mj;
+#pragma unroll
+        for (int off = kMergeChunk / 2; off >= 1; off /= 2) mc = fmaxf(mc, __shfl_xor(mc, off, kWave));
+        const float Mn = fmaxf(M, __shfl(mc, 0, kWave));
+        const float a = exp2_hw((M - Mn) * kLog2e);  // 0 for the first chunk
+        const float w = lane < n ? lj * exp2_hw((mj - Mn) * kLog2e) : 0.f;
+        wsum = wsum * a + w;
+        o0 *= a;
+        o1 *= a;
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+            const float wk = __shfl(w, k, kWave);
+            o0 = __builtin_fmaf(wk, ov[k][0], o0);
+            o1 = __builtin_fmaf(wk, ov[k][1], o1);
         }
+        M = Mn;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off /= 2) wsum += __shfl_xor(wsum, off, kWave);
@@ -463,7 +492,7 @@ static hipError_t launch_decode(const void *q, const void *kc, const void *vc, c
              (float *)(w + up(parts * kDecD * 4) + up(parts * 4))};
     const int G = H / Hkv;
     if (G == 1) {
-        hipLaunchKernelGGL(fa_decode_partition_kernel<T>, dim3(H, S, np), dim3(kDecThreads), 0,
+        hipLaunchKernelGGL(fa_decode_partition_kernel<T>, dim3(H, S, np), dim3(kDecThreads), kDecLdsReserve,
                            stream, (const T *)q, (const T *)kc, (const T *)vc, bt, cl, H, Hkv, MB,
                            np, scale, ws);
     } else {
