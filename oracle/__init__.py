@@ -12,6 +12,7 @@ and widened exactly inside the C code.
 Functions (each cites the page passages it follows in ``oracle.c``):
   attention(q, k, v, scale, causal, rows=None)        dense definition
   attention_ext(q, k, v, scale, causal, window, mask)  rectangular, windowed, masked
+  mask_blocks(mask)                                   block map of a boolean mask
   probs(q, k, scale, causal)                          the full P matrix
   tiled_fa1 / tiled_fa2(q, k, v, scale, causal, Br, Bc)
                                                       the online recurrence in
@@ -75,6 +76,8 @@ def _load():
     lib.oracle_attention_ext.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, d, i, i, i, vp, i64, i64,
                                          vp, i64, vp, vp, i]
     lib.oracle_attention_ext.restype = i
+    lib.oracle_mask_blocks.argtypes = [vp, i, i, i, i, i64, i64, i64, vp]
+    lib.oracle_mask_blocks.restype = i
     lib.oracle_e4m3_encode.argtypes = [vp, i64, vp]
     lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
     lib.oracle_fp8_codes_len.argtypes = [i, i, i, i, i]
@@ -201,6 +204,28 @@ def attention_ext(q, k, v, scale, causal=False, window=(-1, -1), mask=None, rows
                                       _p(o), _p(lse), nthreads or default_threads())
     _check(st, "oracle_attention_ext")
     return o, lse
+
+
+def mask_blocks(mask) -> np.ndarray:
+    """Block map of a boolean / uint8 mask [Bm, Hm, Nq, Nk] (fewer leading dims are
+    broadcast as 1): uint32 [Bm, Hm, ceil(Nq/128), 2, nkw], nkw = ceil(ceil(Nk/64)/32);
+    [.., 0, w] bit i: key block 32w+i of that query block holds a nonzero byte,
+    [.., 1, w] bit i: it holds no zero byte."""
+    m = np.asarray(mask.cpu() if isinstance(mask, torch.Tensor) else mask)
+    while m.ndim < 4:
+        m = m[None]
+    Bm, Hm, Nq, Nk = m.shape
+    # rows padded with a nonzero byte past Nk: padding must not count
+    ld = (Nk + 15) // 16 * 16 + 16
+    buf = np.full((Bm, Hm, Nq, ld), 7, dtype=np.uint8)
+    buf[..., :Nk] = (m != 0).astype(np.uint8) * np.where(np.arange(Nk) % 3 == 0, 1, 255).astype(np.uint8)
+    buf = np.ascontiguousarray(buf)
+    nqb, nkw = (Nq + 127) // 128, ((Nk + 63) // 64 + 31) // 32
+    out = np.zeros((Bm, Hm, nqb, 2, nkw), dtype=np.uint32)
+    lib = _load()
+    _check(lib.oracle_mask_blocks(buf.ctypes.data, Bm, Hm, Nq, Nk, Hm * Nq * ld, Nq * ld, ld,
+                                  out.ctypes.data), "oracle_mask_blocks")
+    return out
 
 
 def attention_bwd(q, k, v, dout, scale, causal, rows=None, keys=None, nthreads=None):

@@ -1085,3 +1085,49 @@ int oracle_attention_ext(const void *q, const void *k, const void *v, int dtype,
     /* scratch: Nk scores + Nk key indices (int64 stored in doubles' space) */
     return or_parallel(or_ext_item, &x, (int64_t)B * H * nrows, 2 * (int64_t)Nk, nthreads);
 }
+
+/* ------------------------------------------------------------------ */
+/* Block map of a boolean mask                                          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The boolean attn_mask of "FlashAttention: GPU 메모리 계층을 활용한 어텐션
+ * 최적화 분석" (youngju.dev), section 11.3, summarised per block of 128 query
+ * rows x 64 keys: which blocks hold a pair that takes part, and which hold no
+ * masked pair.  The pages define the mask only; the map is the forward's
+ * own acceleration structure, and this is its plain definition, block by
+ * block and byte by byte.
+ *
+ * mask: Bs x Hs slices, slice (b, h) at byte b * mask_sb + h * mask_sh, Nq
+ * rows mask_ld bytes apart, of which the first Nk count.  out: uint32 words
+ * [Bs][Hs][ceil(Nq/128)][2][nkw], nkw = ceil(ceil(Nk/64) / 32), written in
+ * full: bit i of word w of the first half is set iff key block 32 w + i has
+ * a nonzero byte among its rows below Nq and keys below Nk; of the second
+ * half, iff it has no zero byte there.  Blocks past Nk keep both bits 0.
+ */
+int oracle_mask_blocks(const uint8_t *mask, int Bs, int Hs, int Nq, int Nk, int64_t mask_sb,
+                       int64_t mask_sh, int64_t mask_ld, uint32_t *out)
+{
+    if (!mask || !out || Bs < 1 || Hs < 1 || Nq < 1 || Nk < 1 || mask_ld < Nk) return -1;
+    if (mask_sb < 0 || mask_sh < 0) return -1;
+    const int nqb = (Nq + 127) / 128, nkb = (Nk + 63) / 64, nkw = (nkb + 31) / 32;
+    for (int b = 0; b < Bs; ++b)
+        for (int h = 0; h < Hs; ++h)
+            for (int qb = 0; qb < nqb; ++qb) {
+                uint32_t *words = out + (((int64_t)b * Hs + h) * nqb + qb) * 2 * nkw;
+                for (int w = 0; w < 2 * nkw; ++w) words[w] = 0;
+                for (int kb = 0; kb < nkb; ++kb) {
+                    int any = 0, all = 1;
+                    for (int i = qb * 128; i < qb * 128 + 128 && i < Nq; ++i)
+                        for (int j = kb * 64; j < kb * 64 + 64 && j < Nk; ++j) {
+                            if (mask[b * mask_sb + h * mask_sh + (int64_t)i * mask_ld + j] != 0)
+                                any = 1;
+                            else
+                                all = 0;
+                        }
+                    if (any) words[kb / 32] |= 1u << (kb % 32);
+                    if (all) words[nkw + kb / 32] |= 1u << (kb % 32);
+                }
+            }
+    return 0;
+}

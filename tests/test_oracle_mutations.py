@@ -4,8 +4,8 @@ Each case copies oracle/oracle.c to a temporary directory, plants one
 plausible mistake (an off-by-one in the causal mask, a dropped scale, log
 base 2, a transposed or wrong operand, a wrong index in the paged layout, a
 wrong sign in an online rescale, ...), builds that copy and runs the pin
-suites (tests/test_oracle_pins.py, test_oracle_decode.py,
-test_oracle_tiling.py) against it in a subprocess.  The mutation passes only
+suites (the tests/test_oracle_*.py files in PIN_SUITES) against it in a
+subprocess.  The mutation passes only
 if at least one pin fails.  A control run of the unmodified copy must pass.
 """
 import concurrent.futures
@@ -19,10 +19,22 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_decode.py",
               "tests/test_oracle_tiling.py", "tests/test_oracle_bwd.py", "tests/test_oracle_fp8.py",
-              "tests/test_oracle_ext.py"]
+              "tests/test_oracle_ext.py", "tests/test_oracle_blocks.py"]
 
 # (name, text in oracle.c, replacement); the text must occur in the source
 MUTATIONS = [
+    ("mask_blocks_last_row_dropped",
+     "for (int i = qb * 128; i < qb * 128 + 128 && i < Nq; ++i)",
+     "for (int i = qb * 128; i < qb * 128 + 127 && i < Nq; ++i)"),
+    ("mask_blocks_halves_swapped",
+     "if (any) words[kb / 32] |= 1u << (kb % 32);",
+     "if (any) words[nkw + kb / 32] |= 1u << (kb % 32);"),
+    ("mask_blocks_row_stride_nk",
+     "(int64_t)i * mask_ld + j] != 0)",
+     "(int64_t)i * Nk + j] != 0)"),
+    ("mask_blocks_key_range_off_by_one",
+     "for (int j = kb * 64; j < kb * 64 + 64 && j < Nk; ++j) {",
+     "for (int j = kb * 64; j < kb * 64 + 64 && j <= Nk; ++j) {"),
     ("causal_mask_excludes_diagonal",
      "int64_t n = x->causal ? (i + 1 < x->N ? i + 1 : x->N) : x->N;",
      "int64_t n = x->causal ? (i < x->N ? i : x->N) : x->N;"),
