@@ -16,7 +16,9 @@ One step = one pass of the whole path over one batch of synthetic input:
      (fwd_fp8), and fa_quant_fp8 of its q, k, v (quant_fp8);
   7. fa_fwd_ext on the forward workload with a causal sliding window of 1024
      keys (fwd_window) and with a block-sparse causal boolean mask
-     (fwd_mask: each (128-query, 64-key) block kept with probability 1/2).
+     (fwd_mask: each (128-query, 64-key) block kept with probability 1/2),
+     and the same mask through its block map (fwd_mask_map: fa_mask_blocks
+     + fa_fwd_ext, the map rebuilt every step).
 Inputs are generated on the host with fixed seeds and copied to HBM before
 the timed region.  The timed region runs K steps between two device
 synchronisations; each kernel call is bracketed by HIP events recorded on the
@@ -207,6 +209,10 @@ def main():
     mask_d = torch.from_numpy(mask_h.astype(np.uint8)).to(dev)
     mask_pairs = int(mask_h.sum())
     del mask_h
+    map_words = fa.fa_mask_blocks_words(B, H, N, N, 0, 0)
+    mask_map = torch.empty(map_words, dtype=torch.int32, device=dev)
+    omb = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    lmb = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     ow = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     lw = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     om = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
@@ -250,13 +256,21 @@ def main():
                       stream=stream)
         if evs:
             evs[9].record(stream)
+        # the same mask through its block map: the map is built every step
+        fa.fa_mask_blocks(mask_d, B, H, N, N, 0, 0, N, mask_map, map_words, stream=stream)
+        if evs:
+            evs[10].record(stream)
+        fa.fa_fwd_ext(qd, kd, vd, omb, lmb, B, H, H, N, N, d, fscale, True, -1, -1, mask_d, 0, 0,
+                      mask_blocks=mask_map, stream=stream)
+        if evs:
+            evs[11].record(stream)
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -296,11 +310,18 @@ def main():
     win_avg, mk_avg = sum(win_ms) / len(win_ms), sum(mk_ms) / len(mk_ms)
     win_tf = win_flops / (win_avg * 1e-3) / 1e12
     mk_tf = mk_flops / (mk_avg * 1e-3) / 1e12
+    map_ms = [e[9].elapsed_time(e[10]) for e in evs]
+    mkb_ms = [e[10].elapsed_time(e[11]) for e in evs]
+    map_avg, mkb_avg = sum(map_ms) / len(map_ms), sum(mkb_ms) / len(mkb_ms)
+    mkb_tf = mk_flops / (mkb_avg * 1e-3) / 1e12
+    mkb_all_tf = mk_flops / ((map_avg + mkb_avg) * 1e-3) / 1e12
+    map_gbs = N * N / (map_avg * 1e-3) / 1e9  # the mask's bytes, read once
 
     # quick sanity of the last step's results (full parity lives in the tests)
     finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item()
                   and torch.isfinite(gout).all().item() and torch.isfinite(go).all().item()
-                  and all(torch.isfinite(t).all().item() for t in (bdq, bdk, bdv, o8, ow, om)))
+                  and all(torch.isfinite(t).all().item() for t in (bdq, bdk, bdv, o8, ow, om))
+                  and (om - omb).abs().max().item() <= 1e-5)
 
     flops = fcfg.flops()
     tflops = flops / (fwd_avg * 1e-3) / 1e12
@@ -418,6 +439,17 @@ def main():
                                   "frac": round(mk_tf / PEAK_BF16_TFLOPS, 4),
                                   "kernel": "fa_fwd_kernel<bf16,128,ext+mask>",
                                   "algorithmic_per_launch": mk_flops}},
+        "fwd_mask_map": {"metric": "attention forward TFLOP/s over visible pairs, boolean mask "
+                                   "with its block map (fa_mask_blocks + fa_fwd_ext)",
+                         "value": round(mkb_all_tf, 2), "unit": "TFLOP/s",
+                         "workload": "the fwd_mask workload, map built every step",
+                         "map_ms_avg": round(map_avg, 4), "map_read_gbs": round(map_gbs, 1),
+                         "kernel_ms_avg": round(mkb_avg, 4),
+                         "roofline": {"bound": "mfma", "achieved": round(mkb_tf, 2),
+                                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(mkb_tf / PEAK_BF16_TFLOPS, 4),
+                                      "kernel": "fa_fwd_kernel<bf16,128,ext+mask> with the map",
+                                      "algorithmic_per_launch": mk_flops}},
         "decode_gqa": {"metric": "paged decode HBM bandwidth, 4 query heads per kv head",
                        "value": round(gqa_gbs, 1), "unit": "GB/s",
                        "workload": gcfg.name, "sum_ctx": int(gctx.sum()),

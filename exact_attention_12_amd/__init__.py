@@ -23,11 +23,13 @@ __all__ = [
     "fa_fwd", "fa_fwd_ext", "forward_ext", "fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_quant_fp8",
     "fa_fwd_fp8", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror", "forward",
     "backward", "quant_fp8", "forward_fp8", "paged_decode", "lib_path", "load_library",
-    "FA_FP8_BLOCK_ROWS",
+    "FA_FP8_BLOCK_ROWS", "FA_MASK_BLOCK_ROWS", "FA_MASK_BLOCK_COLS", "fa_mask_blocks_words",
+    "fa_mask_blocks", "mask_block_map",
 ]
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_DECODE_PARTITION_TOKENS = 256  # must match include/fa.h
+FA_MASK_BLOCK_ROWS, FA_MASK_BLOCK_COLS = 128, 64  # must match include/fa.h
 FA_FP8_BLOCK_ROWS = 128           # must match include/fa.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,9 +67,13 @@ def load_library():
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_gqa.restype = i
     i64 = ctypes.c_int64
-    lib.fa_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, i64, i64, i64, i,
-                               vp]
+    lib.fa_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, i64, i64, i64, vp,
+                               i, vp]
     lib.fa_fwd_ext.restype = i
+    lib.fa_mask_blocks_words.argtypes = [i, i, i, i, i64, i64]
+    lib.fa_mask_blocks_words.restype = sz
+    lib.fa_mask_blocks.argtypes = [vp, i, i, i, i, i64, i64, i64, vp, sz, vp]
+    lib.fa_mask_blocks.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -146,18 +152,37 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype=None, stre
 
 def fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window_left=-1,
                window_right=-1, mask=None, mask_stride_b=0, mask_stride_h=0, mask_ld=None,
-               dtype=None, stream=None):
-    """C entry point ``fa_fwd_ext``: rectangular / windowed / boolean-masked forward."""
+               mask_blocks=None, dtype=None, stream=None):
+    """C entry point ``fa_fwd_ext``: rectangular / windowed / boolean-masked forward
+    (``mask_blocks``: the mask's block map from ``fa_mask_blocks``, or None)."""
     if dtype is None:
         dtype = _dtype_code(q.dtype)
     st = load_library().fa_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                    int(Hkv), int(Nq), int(Nk), int(d), float(scale),
                                    int(bool(causal)), int(window_left), int(window_right),
                                    _ptr(mask), int(mask_stride_b), int(mask_stride_h),
-                                   int(Nk if mask_ld is None else mask_ld), int(dtype),
-                                   _stream(stream))
+                                   int(Nk if mask_ld is None else mask_ld), _ptr(mask_blocks),
+                                   int(dtype), _stream(stream))
     if st != 0:
         raise FAError(st, "fa_fwd_ext")
+
+
+def fa_mask_blocks_words(B, H, Nq, Nk, mask_stride_b, mask_stride_h) -> int:
+    """C entry point ``fa_mask_blocks_words`` (uint32 words of the map; 0 if invalid)."""
+    return int(load_library().fa_mask_blocks_words(int(B), int(H), int(Nq), int(Nk),
+                                                   int(mask_stride_b), int(mask_stride_h)))
+
+
+def fa_mask_blocks(mask, B, H, Nq, Nk, mask_stride_b, mask_stride_h, mask_ld, blocks,
+                   blocks_words=None, stream=None):
+    """C entry point ``fa_mask_blocks``: the block map of a uint8 mask into ``blocks``."""
+    if blocks_words is None:
+        blocks_words = blocks.numel() if isinstance(blocks, torch.Tensor) else 0
+    st = load_library().fa_mask_blocks(_ptr(mask), int(B), int(H), int(Nq), int(Nk),
+                                       int(mask_stride_b), int(mask_stride_h), int(mask_ld),
+                                       _ptr(blocks), int(blocks_words), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_mask_blocks")
 
 
 def fa_bwd_workspace_size(B, H, N) -> int:
@@ -268,10 +293,41 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     return out, lse
 
 
-def forward_ext(q, k, v, scale=None, causal=False, window=(-1, -1), mask=None, stream=None):
+def _padded_mask(mask, B, H, Nq, Nk):
+    """A boolean / uint8 mask broadcastable to [B, H, Nq, Nk] as the C ABI takes it:
+    uint8 rows padded to a multiple of 16 bytes.  Returns (mask, stride_b, stride_h, ld)."""
+    m = mask
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    if m.shape[2:] != (Nq, Nk) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
+        raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
+    # rows padded to a multiple of 16 bytes, as the kernel streams 16-byte chunks
+    ldm = (Nk + 15) // 16 * 16
+    padded = torch.zeros(m.shape[:3] + (ldm,), dtype=torch.uint8, device=m.device)
+    padded[..., :Nk] = m.to(torch.uint8)
+    sb = 0 if m.shape[0] == 1 else m.shape[1] * Nq * ldm
+    sh = 0 if m.shape[1] == 1 else Nq * ldm
+    _check_dev("mask", padded, torch.uint8)
+    return padded, sb, sh, ldm
+
+
+def mask_block_map(mask, B, H, Nq, Nk, stream=None):
+    """Block map (``fa_mask_blocks``) of a boolean / uint8 mask broadcastable to
+    [B, H, Nq, Nk], as an int32 tensor to pass to ``forward_ext(block_map=...)``."""
+    padded, sb, sh, ldm = _padded_mask(mask, B, H, Nq, Nk)
+    words = fa_mask_blocks_words(B, H, Nq, Nk, sb, sh)
+    blocks = torch.empty(words, dtype=torch.int32, device=padded.device)
+    fa_mask_blocks(padded, B, H, Nq, Nk, sb, sh, ldm, blocks, words, stream=stream)
+    return blocks
+
+
+def forward_ext(q, k, v, scale=None, causal=False, window=(-1, -1), mask=None, block_map=None,
+                stream=None):
     """Allocate o, lse and run ``fa_fwd_ext``: q [B, H, Nq, d], k, v [B, Hkv, Nk, d], a
     bottom-right aligned causal mask, a (left, right) window (-1 = unbounded) and an
-    optional boolean / uint8 mask broadcastable to [B, H, Nq, Nk] (True = takes part)."""
+    optional boolean / uint8 mask broadcastable to [B, H, Nq, Nk] (True = takes part).
+    block_map: None, True (compute the mask's block map first) or the tensor that
+    ``mask_block_map`` returned for this mask."""
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(n, t, q.dtype)
     B, H, Nq, d = q.shape
@@ -281,24 +337,25 @@ def forward_ext(q, k, v, scale=None, causal=False, window=(-1, -1), mask=None, s
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     sb = sh = 0
+    ldm = None
+    blocks = None
     if mask is not None:
-        m = mask
-        while m.dim() < 4:
-            m = m.unsqueeze(0)
-        if m.shape[2:] != (Nq, Nk) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
-            raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
-        # rows padded to a multiple of 16 bytes, as the kernel streams 16-byte chunks
-        ldm = (Nk + 15) // 16 * 16
-        padded = torch.zeros(m.shape[:3] + (ldm,), dtype=torch.uint8, device=m.device)
-        padded[..., :Nk] = m.to(torch.uint8)
-        mask = padded
-        sb = 0 if m.shape[0] == 1 else m.shape[1] * Nq * ldm
-        sh = 0 if m.shape[1] == 1 else Nq * ldm
-        _check_dev("mask", mask, torch.uint8)
+        mask, sb, sh, ldm = _padded_mask(mask, B, H, Nq, Nk)
+        if block_map is True:
+            blocks = torch.empty(fa_mask_blocks_words(B, H, Nq, Nk, sb, sh), dtype=torch.int32,
+                                 device=mask.device)
+            fa_mask_blocks(mask, B, H, Nq, Nk, sb, sh, ldm, blocks, stream=stream)
+        elif block_map is not None:
+            blocks = block_map
+            if blocks.numel() < fa_mask_blocks_words(B, H, Nq, Nk, sb, sh):
+                raise ValueError("block_map is smaller than the map of this mask")
+            _check_dev("block_map", blocks, torch.int32)
+    elif block_map is not None:
+        raise ValueError("block_map needs a mask")
     o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window[0], window[1], mask,
-               sb, sh, None if mask is None else mask.shape[-1], stream=stream)
+               sb, sh, ldm, mask_blocks=blocks, stream=stream)
     return o, lse
 
 

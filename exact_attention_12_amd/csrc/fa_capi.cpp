@@ -26,8 +26,11 @@ hipError_t bwd_dispatch(const void *q, const void *k, const void *v, const float
 size_t bwd_workspace_bytes(int B, int H, int N);
 hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
                             int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int wl,
-                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int ldm, int dtype,
-                            hipStream_t stream);
+                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int ldm,
+                            const uint32_t *blocks, int dtype, hipStream_t stream);
+size_t mask_blocks_words(int B, int H, int Nq, int Nk, int64_t msb, int64_t msh);
+hipError_t mask_blocks_dispatch(const uint8_t *mask, int B, int H, int Nq, int Nk, int64_t msb,
+                                int64_t msh, int ldm, uint32_t *blocks, hipStream_t stream);
 hipError_t quant_fp8_dispatch(const void *x, int dtype, int B, int H, int N, int d, int layout,
                               void *codes, int32_t *exps, hipStream_t stream);
 hipError_t fwd_fp8_dispatch(const void *q8, const void *k8, const void *v8, const int32_t *qe,
@@ -112,17 +115,61 @@ extern "C" int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o,
     return fwd_checked(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype, stream);
 }
 
+// The mask arguments shared by fa_fwd_ext and fa_mask_blocks (mask not null).
+static int check_mask(const uint8_t *mask, int Nq, int Nk, int64_t msb, int64_t msh, int64_t ldm)
+{
+    if (msb < 0 || msh < 0 || ldm < Nk) return FA_ERR_INVALID_ARG;
+    if ((int64_t)Nq * ldm > INT_MAX) return FA_ERR_UNSUPPORTED;  // one mask slice < 2 GiB
+    if (!aligned(mask, 16) || ldm % 16 || msb % 16 || msh % 16) return FA_ERR_ALIGNMENT;
+    return FA_OK;
+}
+
+// bytes from the mask's first slice to the end of its last
+static uint64_t mask_extent(int B, int H, int Nq, int64_t msb, int64_t msh, int64_t ldm)
+{
+    return (uint64_t)(B - 1) * msb + (uint64_t)(H - 1) * msh + (uint64_t)Nq * ldm;
+}
+
+extern "C" size_t fa_mask_blocks_words(int B, int H, int Nq, int Nk, int64_t mask_stride_b,
+                                       int64_t mask_stride_h)
+{
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || mask_stride_b < 0 || mask_stride_h < 0) return 0;
+    return fa::mask_blocks_words(B, H, Nq, Nk, mask_stride_b, mask_stride_h);
+}
+
+extern "C" int fa_mask_blocks(const uint8_t *mask, int B, int H, int Nq, int Nk, int64_t mask_stride_b,
+                              int64_t mask_stride_h, int64_t mask_ld, uint32_t *blocks,
+                              size_t blocks_words, void *stream)
+{
+    if (!mask || !blocks) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_INVALID_ARG;
+    const int mc = check_mask(mask, Nq, Nk, mask_stride_b, mask_stride_h, mask_ld);
+    if (mc != FA_OK) return mc;
+    if (!aligned(blocks, 4)) return FA_ERR_ALIGNMENT;
+    const size_t words = fa::mask_blocks_words(B, H, Nq, Nk, mask_stride_b, mask_stride_h);
+    if (blocks_words < words) return FA_ERR_INVALID_ARG;
+    // one workgroup per (slice, 128-row block, 2048 keys)
+    if (words / 2 > (size_t)INT_MAX) return FA_ERR_UNSUPPORTED;
+    if (overlap(blocks, (uint64_t)words * 4, mask,
+                mask_extent(B, H, Nq, mask_stride_b, mask_stride_h, mask_ld)))
+        return FA_ERR_INVALID_ARG;
+    const hipError_t e = fa::mask_blocks_dispatch(mask, B, H, Nq, Nk, mask_stride_b, mask_stride_h,
+                                                  (int)mask_ld, blocks, (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" int fa_fwd_ext(const void *q, const void *k, const void *v, float *o, float *lse, int B,
                           int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                           int window_left, int window_right, const uint8_t *mask,
-                          int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_ld, int dtype,
-                          void *stream)
+                          int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_ld,
+                          const uint32_t *mask_blocks, int dtype, void *stream)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
     if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
     if (mask && (mask_stride_b < 0 || mask_stride_h < 0 || mask_ld < Nk)) return FA_ERR_INVALID_ARG;
+    if (mask_blocks && !mask) return FA_ERR_INVALID_ARG;
     const int es = elem_bytes(dtype);
     if (es == 0) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -135,20 +182,22 @@ extern "C" int fa_fwd_ext(const void *q, const void *k, const void *v, float *o,
         return FA_ERR_ALIGNMENT;
     if (mask && (!aligned(mask, 16) || mask_ld % 16 || mask_stride_b % 16 || mask_stride_h % 16))
         return FA_ERR_ALIGNMENT;
+    if (mask_blocks && !aligned(mask_blocks, 4)) return FA_ERR_ALIGNMENT;
     const uint64_t rows = (uint64_t)B * H * Nq, kv_rows = (uint64_t)B * Hkv * Nk;
     const uint64_t o_bytes = rows * d * 4, l_bytes = rows * 4;
-    const uint64_t m_bytes =
-        mask ? (uint64_t)(B - 1) * mask_stride_b + (uint64_t)(H - 1) * mask_stride_h + (uint64_t)Nq * mask_ld : 0;
+    const uint64_t m_bytes = mask ? mask_extent(B, H, Nq, mask_stride_b, mask_stride_h, mask_ld) : 0;
+    const uint64_t mb_bytes =
+        mask_blocks ? (uint64_t)fa::mask_blocks_words(B, H, Nq, Nk, mask_stride_b, mask_stride_h) * 4 : 0;
     if (overlap(o, o_bytes, lse, l_bytes)) return FA_ERR_INVALID_ARG;
-    const void *ins[4] = {q, k, v, mask};
-    const uint64_t in_bytes[4] = {rows * d * es, kv_rows * d * es, kv_rows * d * es, m_bytes};
-    for (int i = 0; i < 4; ++i)
+    const void *ins[5] = {q, k, v, mask, mask_blocks};
+    const uint64_t in_bytes[5] = {rows * d * es, kv_rows * d * es, kv_rows * d * es, m_bytes, mb_bytes};
+    for (int i = 0; i < 5; ++i)
         if (ins[i] && (overlap(o, o_bytes, ins[i], in_bytes[i]) || overlap(lse, l_bytes, ins[i], in_bytes[i])))
             return FA_ERR_INVALID_ARG;
     const hipError_t e =
         fa::fwd_ext_dispatch(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, window_left,
-                             window_right, mask, mask_stride_b, mask_stride_h, (int)mask_ld, dtype,
-                             (hipStream_t)stream);
+                             window_right, mask, mask_stride_b, mask_stride_h, (int)mask_ld,
+                             mask_blocks, dtype, (hipStream_t)stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -79,11 +79,17 @@ struct FwdExt {
     const uint8_t *mask;  // uint8 [.., Nq, ldm] or null
     int64_t msb, msh;     // byte strides of the mask between batches and heads
     int ldm;              // byte stride between mask rows (a multiple of 16, >= Nk)
+    // Block map of the mask (fa_mask_blocks) or null.  Per (slice, 128-row
+    // query block): nkw words with bit k set if 64-key block k holds a
+    // visible pair, then nkw words with bit k set if it holds no masked one.
+    const uint32_t *blocks;
+    int nkw;              // words per half of a query block's entry
+    int64_t bmb, bmh;     // word strides of the map between batches and heads
 };
 
 // EXT: 0 = square path (N queries and keys, optional top-left causal mask),
 // 1 = general ranges (rectangular / windowed / bottom-right causal), 2 = 1
-// plus a boolean mask.
+// plus a boolean mask, 3 = 2 with the mask's block map.
 template <typename T, int D, bool CAUSAL, int EXT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(FwdCfg<T, D>::WPE, FwdCfg<T, D>::WPE)))
@@ -94,14 +100,15 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     static_assert(EXT == 0 || !CAUSAL, "general masks fold causality into the window");
     const int NK = EXT ? ext.Nk : N;  // keys
     using C = FwdCfg<T, D>;
+    static_assert(C::BR == 128 && 64 % C::BC == 0, "a block of the mask's map (128 x 64) is whole tiles");
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int KW = C::KW;
     // boolean mask: a (BR x BC)-byte tile of it rides along with each K/V tile,
     // rows of BC bytes with the 16-byte chunks swizzled by swzm()
     constexpr int MCPR = C::BC / 16;                            // 16-byte chunks per mask row
-    constexpr int MASKB = EXT == 2 ? C::BR * C::BC : 0;         // mask tile bytes
-    constexpr int NLDM_W = EXT == 2 ? C::BR * MCPR / kWave / 4 : 0;  // its 1 KiB loads per wave
+    constexpr int MASKB = EXT >= 2 ? C::BR * C::BC : 0;         // mask tile bytes
+    constexpr int NLDM_W = EXT >= 2 ? C::BR * MCPR / kWave / 4 : 0;  // its 1 KiB loads per wave
     constexpr int SB = C::STAGEB + MASKB;                        // bytes per stage
     auto swzm = [](int row) { return MCPR == 4 ? (row >> 2) & 3 : (row >> 3) & 1; };
     __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
@@ -159,9 +166,9 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)Kh, 0, head_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)Vh, 0, head_bytes, kBufferFlags);
     const uint8_t *mbase = nullptr;
-    if constexpr (EXT == 2) mbase = ext.mask + (int64_t)(bh / H) * ext.msb + (int64_t)(bh % H) * ext.msh;
+    if constexpr (EXT >= 2) mbase = ext.mask + (int64_t)(bh / H) * ext.msb + (int64_t)(bh % H) * ext.msh;
     const __amdgpu_buffer_rsrc_t mrs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)mbase, 0, EXT == 2 ? N * ext.ldm : 0, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void *)mbase, 0, EXT >= 2 ? N * ext.ldm : 0, kBufferFlags);
     // per-lane mask-tile load offsets (set per query tile): load I, lane l
     // fills chunk position p = I*64 + l = row p / MCPR, position p % MCPR
     // holding chunk (p % MCPR) ^ swzm(row) of mask row q0 + row
@@ -174,7 +181,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             m_off[i] = (q0_ + row) * ext.ldm + ((p % MCPR) ^ swzm(row)) * 16;
         }
     };
-    auto load_tile = [&](int j, int buf) {
+    auto load_tile = [&](int j, int buf, bool with_mask) {
         const int k0 = j * C::BC;
         char *kd = smem + buf * SB;
         char *vd = kd + C::TILEB;
@@ -197,11 +204,13 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                 buffer_load_lds16(vrs, vd + I * 1024, off, soff);
             }
         }
-        if constexpr (EXT == 2) {
+        if constexpr (EXT >= 2) {
             // rows past the end of the mask read as 0 (buffer bounds)
+            if (with_mask) {
 #pragma unroll
-            for (int i = 0; i < NLDM_W; ++i)
-                buffer_load_lds16(mrs, kd + C::STAGEB + (wave * NLDM_W + i) * 1024, m_off[i], k0);
+                for (int i = 0; i < NLDM_W; ++i)
+                    buffer_load_lds16(mrs, kd + C::STAGEB + (wave * NLDM_W + i) * 1024, m_off[i], k0);
+            }
         }
     };
     // byte offset of element e of row r in a swizzled tile
@@ -239,7 +248,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // K operands are read from LDS in groups of two steps, one group
     // ahead of the matrix products that use them.
     auto qk = [&](const char *Ks, f32x16 (&s)[C::NKB]) {
-        constexpr int G = EXT == 2 ? 1 : 2;  // registers for the boolean mask
+        constexpr int G = EXT >= 2 ? 1 : 2;  // registers for the boolean mask
         constexpr int NG = C::QK_STEPS / G;
         frag kf[2][G][C::NKB];
         auto rd = [&](int g, int b) {
@@ -304,7 +313,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             for (int r = 0; r < 16; ++r) {
                 bool off_ = acc_row(r, 0) > lim[kb];
                 if constexpr (EXT != 0) off_ = off_ || acc_row(r, 0) < lo[kb];
-                if constexpr (EXT == 2) off_ = off_ || ((mw[kb][r / 4] >> (8 * (r % 4))) & 0xffu) == 0;
+                if constexpr (EXT >= 2) off_ = off_ || ((mw[kb][r / 4] >> (8 * (r % 4))) & 0xffu) == 0;
                 if (off_) s[kb][r] = -INFINITY;
                 else bits |= 1u << (kb * 16 + r);
             }
@@ -355,25 +364,41 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         return (part[0] + part[1]) + (part[2] + part[3]);
     };
 
-    // One K/V tile: j is the tile, STAGE (= j % 2) its LDS buffer.
-    auto tile = [&](int j, auto stage_c) {
+    // One K/V tile: j is the tile, STAGE its LDS buffer; jn is the tile to
+    // load next (ntiles: none).  Boolean mask: part (part_n) tells whether
+    // tile j (jn) needs its mask bytes; without them it is fully visible.
+    auto tile = [&](int j, int jn, bool part, bool part_n, auto stage_c) {
         constexpr int STAGE = decltype(stage_c)::value;
         const int k0 = j * C::BC;
-        if (j + 1 < ntiles) load_tile(j + 1, STAGE ^ 1);
+        if (jn < ntiles) load_tile(jn, STAGE ^ 1, part_n);
         uint32_t mcur[C::NKB][4];
-        if constexpr (EXT == 2) read_mask(smem + STAGE * SB + C::STAGEB, mcur);
+        if constexpr (EXT >= 2) {
+            if (part) {
+                read_mask(smem + STAGE * SB + C::STAGEB, mcur);
+            } else {
+                // every pair of the block takes part; rows past the end stay
+                // masked, as the mask bytes read for them are 0
+                const uint32_t all = qrow < N ? 0xffffffffu : 0u;
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) mcur[kb][g] = all;
+            }
+        }
         const char *Ks = smem + STAGE * SB;
         const char *Vs = Ks + C::TILEB;
 
         bool skip = EXT != 0 && (j < jw_beg || j >= jw_end);  // no row of the wave sees a key here
-        if constexpr (EXT == 2) {
+        if constexpr (EXT >= 2) {
             // ... or the mask hides every key of the tile from every row of the wave
-            uint32_t any = 0;
+            if (part) {
+                uint32_t any = 0;
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
+                for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) any |= mcur[kb][g];
-            skip = skip || __builtin_amdgcn_ballot_w64(any != 0) == 0;
+                    for (int g = 0; g < 4; ++g) any |= mcur[kb][g];
+                skip = skip || __builtin_amdgcn_ballot_w64(any != 0) == 0;
+            }
         }
         if (skip) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -383,10 +408,10 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         f32x16 s[C::NKB];
         qk(Ks, s);
         bool need_mask = (k0 + C::BC > NK) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
-        if constexpr (EXT == 1)
+        if constexpr (EXT != 0)
             need_mask = k0 < min(wq_hi, N - 1) + ext.off - ext.wl ||
                         k0 + C::BC - 1 > min(wq_lo + ext.off + ext.wr, NK - 1);
-        if constexpr (EXT == 2) need_mask = true;
+        if constexpr (EXT >= 2) need_mask = need_mask || part || wq_hi >= N;
         int lim[C::NKB], lo[C::NKB];
         limits(k0, lim, lo);
         uint32_t vis = 0;
@@ -402,13 +427,18 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         // probability, keeping it representable even in fp16) recompute the
         // tile's scores and move the reference.
         // General masks: a row may see no key of its first tiles, so the
-        // reference is (re)set while any row of the wave has none yet.
-        if (EXT == 0 ? j == 0 : __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0) rebase(s);
+        // reference is (re)set while any row of the wave has none yet.  With
+        // a boolean mask, rows past the end see no key at all and take no
+        // part in that decision (their mc_ref starts at 0, so that their
+        // probabilities come out as exp2(-inf) = 0 without a reference).
+        if (EXT == 0 ? j == 0
+                     : __builtin_amdgcn_ballot_w64(m_ref == -INFINITY && (EXT < 2 || qrow < N)) != 0)
+            rebase(s);
         float rs = exponentiate(s);
         if ((EXT != 0 || j != 0) && __builtin_amdgcn_ballot_w64(!(rs <= kPMax)) != 0) {
             qk(Ks, s);
             if (need_mask) {
-                if constexpr (EXT == 2) apply_bits(s, vis);
+                if constexpr (EXT >= 2) apply_bits(s, vis);
                 else apply_mask(s, lim, lo, mcur);
             }
             rebase(s);
@@ -492,40 +522,98 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         const int kw_end = min(NK, w_last + ext.off + ext.wr + 1);
         jw_beg = kw_beg / C::BC;
         jw_end = (wq_lo < N && kw_end > kw_beg) ? (kw_end + C::BC - 1) / C::BC : 0;
-        if constexpr (EXT == 2) set_mask_offsets(q0);
+        if constexpr (EXT >= 2) set_mask_offsets(q0);
     }
     ntiles = kend > jbeg * C::BC ? (kend + C::BC - 1) / C::BC : jbeg;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
     m_ref = -INFINITY;
-    mc_ref = -INFINITY;
+    mc_ref = EXT >= 2 ? 0.f : -INFINITY;
     l_run = 0.f;
     l_hat = 0.f;
 
-    if (jbeg < ntiles) {
-        load_tile(jbeg, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
+    if constexpr (EXT == 3) {
+        // Boolean mask with its block map: tiles whose 64-key block holds no
+        // visible pair for this query block are never loaded, and tiles whose
+        // block holds no masked pair skip the mask bytes; the tiles left run
+        // in key order, alternating LDS buffers.  The map's words are read
+        // with scalar loads, one word (32 blocks) at a time.
+        const uint32_t *mrow = ext.blocks + (int64_t)(bh / H) * ext.bmb + (int64_t)(bh % H) * ext.bmh +
+                               (int64_t)qt * 2 * ext.nkw;
+        int wi = -1;
+        uint32_t w_any = 0, w_full = 0;
+        auto word = [&](int w) {
+            if (w != wi) {
+                wi = w;
+                w_any = mrow[w];
+                w_full = mrow[ext.nkw + w];
+            }
+        };
+        // first tile after jj that the map does not rule out (ntiles: none)
+        auto next = [&](int jj) {
+            int jn = jj + 1;
+            while (jn < ntiles) {
+                const int bl = jn * C::BC / 64;
+                word(bl / 32);
+                const uint32_t rest = w_any >> (bl % 32);
+                if (rest & 1u) return jn;
+                jn = (rest ? bl + (int)__builtin_ctz(rest) : (bl / 32 + 1) * 32) * 64 / C::BC;
+            }
+            return ntiles;
+        };
+        auto partial = [&](int jj) {
+            if (jj >= ntiles) return true;
+            const int bl = jj * C::BC / 64;
+            word(bl / 32);
+            return ((w_full >> (bl % 32)) & 1u) == 0;
+        };
+        int j = next(jbeg - 1);
+        bool part = partial(j);
+        if (j < ntiles) {
+            load_tile(j, 0, part);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        while (j < ntiles) {
+            int jn = next(j);
+            bool pn = partial(jn);
+            tile(j, jn, part, pn, std::integral_constant<int, 0>{});
+            j = jn;
+            part = pn;
+            if (j >= ntiles) break;
+            jn = next(j);
+            pn = partial(jn);
+            tile(j, jn, part, pn, std::integral_constant<int, 1>{});
+            j = jn;
+            part = pn;
+        }
+    } else {
+        if (jbeg < ntiles) {
+            load_tile(jbeg, 0, EXT == 2);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
 
-    // Causal: this wave's rows see no key of tiles j >= nt_w; those tiles are
-    // still loaded for the other waves (same barrier count for every wave).
-    // General masks: every tile of the workgroup's range runs through tile(),
-    // which skips the arithmetic for the wave's tiles outside [jw_beg, jw_end).
-    const int nt_w = CAUSAL ? min(ntiles, wq_hi / C::BC + 1) : ntiles;
-    int j = jbeg;
-    for (; j + 1 < nt_w; j += 2) {
-        tile(j, std::integral_constant<int, 0>{});
-        tile(j + 1, std::integral_constant<int, 1>{});
-    }
-    if (j < nt_w) {
-        tile(j, std::integral_constant<int, 0>{});
-        ++j;
-    }
-    for (; j < ntiles; ++j) {
-        if (j + 1 < ntiles) load_tile(j + 1, (j + 1 - jbeg) & 1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // Causal: this wave's rows see no key of tiles j >= nt_w; those tiles
+        // are still loaded for the other waves (same barrier count for every
+        // wave).  General masks: every tile of the workgroup's range runs
+        // through tile(), which skips the arithmetic for the wave's tiles
+        // outside [jw_beg, jw_end).
+        const int nt_w = CAUSAL ? min(ntiles, wq_hi / C::BC + 1) : ntiles;
+        int j = jbeg;
+        for (; j + 1 < nt_w; j += 2) {
+            tile(j, j + 1, true, true, std::integral_constant<int, 0>{});
+            tile(j + 1, j + 2, true, true, std::integral_constant<int, 1>{});
+        }
+        if (j < nt_w) {
+            tile(j, j + 1, true, true, std::integral_constant<int, 0>{});
+            ++j;
+        }
+        for (; j < ntiles; ++j) {
+            if (j + 1 < ntiles) load_tile(j + 1, (j + 1 - jbeg) & 1, EXT == 2);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: O = acc / l, lse = scale*m + ln l ----------------------
@@ -560,7 +648,7 @@ static hipError_t launch_fwd(const void *q, const void *k, const void *v, float 
     const int64_t grid = (int64_t)B * H * (CAUSAL ? (nqt + 1) / 2 : nqt);
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 0>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, o, lse, N, nqt, scale, H, H / Hkv,
-                       FwdExt{N, 0, 0, 0, nullptr, 0, 0, 0});
+                       FwdExt{N, 0, 0, 0, nullptr, 0, 0, 0, nullptr, 0, 0, 0});
     return hipGetLastError();
 }
 
@@ -572,7 +660,10 @@ static hipError_t launch_fwd_ext(const void *q, const void *k, const void *v, fl
     using C = FwdCfg<T, D>;
     const int nqt = (Nq + C::BR - 1) / C::BR;
     const int64_t grid = (int64_t)B * H * nqt;
-    if (ext.mask)
+    if (ext.mask && ext.blocks)
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, 3>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                           (const T *)q, (const T *)k, (const T *)v, o, lse, Nq, nqt, scale, H, H / Hkv, ext);
+    else if (ext.mask)
         hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, 2>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
                            (const T *)q, (const T *)k, (const T *)v, o, lse, Nq, nqt, scale, H, H / Hkv, ext);
     else
@@ -611,19 +702,130 @@ hipError_t fwd_dispatch(const void *q, const void *k, const void *v, float *o, f
     }
 }
 
+// Shape of the block map of a mask (see FwdExt::blocks): query blocks of
+// kMapRows rows, key blocks of kMapCols keys, 32 key blocks per word; the
+// map of slice (b, h) is shared along a dimension the mask broadcasts over.
+constexpr int kMapRows = 128, kMapCols = 64;
+struct MapShape {
+    int nqb, nkw, Bs, Hs;
+    int64_t bmb, bmh;  // word strides between batches and heads (0: broadcast)
+};
+MapShape map_shape(int B, int H, int Nq, int Nk, int64_t msb, int64_t msh)
+{
+    MapShape m;
+    m.nqb = (Nq + kMapRows - 1) / kMapRows;
+    m.nkw = ((Nk + kMapCols - 1) / kMapCols + 31) / 32;
+    m.Bs = msb ? B : 1;
+    m.Hs = msh ? H : 1;
+    m.bmh = msh ? (int64_t)m.nqb * 2 * m.nkw : 0;
+    m.bmb = msb ? (int64_t)m.Hs * m.nqb * 2 * m.nkw : 0;
+    return m;
+}
+
+// x has a zero byte
+__device__ __forceinline__ bool zero_byte(uint32_t x) { return ((x - 0x01010101u) & ~x & 0x80808080u) != 0; }
+
+// Block map of a boolean mask: one workgroup per (slice, query block qb,
+// word w of 32 key blocks = 2048 keys).  Thread t reads the 16-byte chunk
+// (t % 128) of the word's keys in the 64 rows qb*128 + 64*(t / 128) + ..;
+// bytes past Nk and rows past Nq do not count.  Bit i of the "any" word:
+// key block 32w + i holds a nonzero byte; of the "full" word: it holds no
+// zero byte (and at least one byte, so full implies any).
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void fa_mask_blocks_kernel(const uint8_t *__restrict__ mask, int Hs, int Nq, int Nk, int64_t msb,
+                           int64_t msh, int ldm, int nqb, int nkw, uint32_t *__restrict__ blocks)
+{
+    const int wid = blockIdx.x;
+    const int w = wid % nkw, qb = (wid / nkw) % nqb, slice = wid / (nkw * nqb);
+    const uint8_t *base = mask + (int64_t)(slice / Hs) * msb + (int64_t)(slice % Hs) * msh;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int c = (wave % 2) * kWave + lane;
+    const int r0 = qb * kMapRows + (wave / 2) * 64;
+    const int key0 = w * 32 * kMapCols + c * 16;
+    const int nvalid = min(max(Nk - key0, 0), 16);  // bytes of the chunk inside the key range
+    const int nrows = min(64, Nq - r0);
+    uint32_t keep[4];  // 0xff on the bytes inside the key range
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int nb = min(max(nvalid - 4 * i, 0), 4);
+        keep[i] = nb == 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u;
+    }
+    bool any = false, all = true;
+    if (nvalid > 0 && nrows > 0) {
+        const uint8_t *p = base + (int64_t)r0 * ldm + key0;
+        for (int r = 0; r < nrows; r += 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (r + k < nrows) v[k] = *(const u32x4 *)(p + (int64_t)(r + k) * ldm);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (r + k < nrows) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        any = any || (v[k][i] & keep[i]) != 0;
+                        all = all && !zero_byte(v[k][i] | ~keep[i]);
+                    }
+                }
+        }
+    }
+    // key block i of the wave's 64 chunks: lanes 4i .. 4i+3
+    const uint64_t A = __builtin_amdgcn_ballot_w64(any), L = __builtin_amdgcn_ballot_w64(all);
+    uint32_t ba = 0, bl = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if ((A >> (4 * i)) & 0xfu) ba |= 1u << i;
+        if (((L >> (4 * i)) & 0xfu) == 0xfu) bl |= 1u << i;
+    }
+    __shared__ uint32_t sa[4], sl[4];
+    if (lane == 0) {
+        sa[wave] = ba;
+        sl[wave] = bl;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t a = (sa[0] | sa[2]) | ((sa[1] | sa[3]) << 16);
+        const uint32_t f = (sl[0] & sl[2]) | ((sl[1] & sl[3]) << 16);
+        uint32_t *out = blocks + ((int64_t)slice * nqb + qb) * 2 * nkw;
+        out[w] = a;
+        out[nkw + w] = f & a;
+    }
+}
+
+size_t mask_blocks_words(int B, int H, int Nq, int Nk, int64_t msb, int64_t msh)
+{
+    const MapShape m = map_shape(B, H, Nq, Nk, msb, msh);
+    return (size_t)m.Bs * m.Hs * m.nqb * 2 * m.nkw;
+}
+
+// Arguments validated by the caller (the mask as for fwd_ext_dispatch; the
+// grid below fits an int).
+hipError_t mask_blocks_dispatch(const uint8_t *mask, int B, int H, int Nq, int Nk, int64_t msb,
+                                int64_t msh, int ldm, uint32_t *blocks, hipStream_t stream)
+{
+    const MapShape m = map_shape(B, H, Nq, Nk, msb, msh);
+    const int64_t grid = (int64_t)m.Bs * m.Hs * m.nqb * m.nkw;
+    hipLaunchKernelGGL(fa_mask_blocks_kernel, dim3((unsigned)grid), dim3(256), 0, stream, mask, m.Hs, Nq,
+                       Nk, msb, msh, ldm, m.nqb, m.nkw, blocks);
+    return hipGetLastError();
+}
+
 // General masks.  Arguments validated by the caller: Nq, Nk >= 1; wl, wr are
-// the window bounds (< 0 = unbounded); causal limits the right bound to 0.
+// the window bounds (< 0 = unbounded); causal limits the right bound to 0;
+// blocks, if not null, is the mask's block map (mask_blocks_dispatch).
 hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
                             int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int wl,
-                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int ldm, int dtype,
-                            hipStream_t stream)
+                            int wr, const uint8_t *mask, int64_t msb, int64_t msh, int ldm,
+                            const uint32_t *blocks, int dtype, hipStream_t stream)
 {
     // bounds beyond Nq + Nk are unbounded; keep every sum inside int
     const int big = Nq + Nk;
     int r = wr < 0 ? big : min(wr, big);
     if (causal) r = min(r, 0);
     const int l = wl < 0 ? big : min(wl, big);
-    const FwdExt ext{Nk, Nk - Nq, l, r, mask, msb, msh, ldm};
+    const MapShape m = map_shape(B, H, Nq, Nk, msb, msh);
+    const FwdExt ext{Nk, Nk - Nq, l, r, mask, msb, msh, ldm, mask ? blocks : nullptr, m.nkw, m.bmb, m.bmh};
     switch (dtype) {
     case 0:
         return d == 64 ? launch_fwd_ext<float, 64>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream)

@@ -135,14 +135,58 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse
  *               the first Nk are used.  mask, mask_ld and both strides must
  *               be multiples of 16 (else FA_ERR_ALIGNMENT; pad the rows),
  *               mask_ld >= Nk, and Nq * mask_ld below 2^31.
+ *   mask_blocks : NULL, or the block map of this mask that fa_mask_blocks
+ *               wrote for the same B, H, Nq, Nk and strides (4-byte aligned;
+ *               requires a mask, else FA_ERR_INVALID_ARG).  With it, key
+ *               tiles the map marks empty are skipped without being read and
+ *               tiles it marks full skip the mask bytes; the result is the
+ *               same as without it.  A map that does not describe the mask
+ *               (stale, or another mask's) gives wrong results but never
+ *               reads outside q, k, v, the mask or the map.
  *   A row that sees no key gets o = 0 and lse = -inf.
  * Every other argument and the error behaviour are those of fa_fwd_gqa; o
- * and lse must not overlap q, k, v or the mask.
+ * and lse must not overlap q, k, v, the mask or its map.
  */
 int fa_fwd_ext(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
                int Hkv, int Nq, int Nk, int d, float scale, int causal, int window_left,
                int window_right, const uint8_t *mask, int64_t mask_stride_b, int64_t mask_stride_h,
-               int64_t mask_ld, int dtype, void *stream);
+               int64_t mask_ld, const uint32_t *mask_blocks, int dtype, void *stream);
+
+/*
+ * Block map of a boolean mask, for fa_fwd_ext: which blocks of
+ * FA_MASK_BLOCK_ROWS query rows x FA_MASK_BLOCK_COLS keys hold a visible
+ * pair, and which hold no masked one.  The map is this library's own
+ * acceleration structure for the boolean attn_mask of youngju.dev section
+ * 11.3 (the pages define the mask, not the map): a mask that is reused
+ * (across heads, layers or steps) is summarised once.
+ *
+ * Layout: uint32 words [Bs][Hs][ceil(Nq / 128)][2][nkw], with Bs = B if
+ * mask_stride_b != 0 else 1, Hs likewise from H and mask_stride_h, and
+ * nkw = ceil(ceil(Nk / 64) / 32).  For slice (b, h) and query block qb,
+ * bit i of word w of the first half is set iff key block kb = 32 w + i
+ * holds a nonzero mask byte (rows qb*128 .. +127 below Nq, keys kb*64 ..
+ * +63 below Nk); of the second half, iff it holds no zero byte there (and
+ * lies inside the key range).  Bits of blocks past Nk are 0.
+ */
+#define FA_MASK_BLOCK_ROWS 128
+#define FA_MASK_BLOCK_COLS 64
+
+/* Words of the block map for these sizes and strides (0 for invalid sizes). */
+size_t fa_mask_blocks_words(int B, int H, int Nq, int Nk, int64_t mask_stride_b,
+                            int64_t mask_stride_h);
+
+/*
+ * fa_mask_blocks -- write the block map of a mask (layout above).
+ *   mask, B, H, Nq, Nk, mask_stride_b, mask_stride_h, mask_ld : as in
+ *               fa_fwd_ext (mask not NULL), with its checks and error codes.
+ *   blocks    : device, 4-byte aligned, blocks_words >= fa_mask_blocks_words
+ *               (else FA_ERR_INVALID_ARG); must not overlap the mask.
+ *   stream    : hipStream_t or NULL; the map is ready in stream order.
+ * Returns FA_ERR_UNSUPPORTED when Bs * Hs * ceil(Nq/128) * nkw >= 2^31.
+ */
+int fa_mask_blocks(const uint8_t *mask, int B, int H, int Nq, int Nk, int64_t mask_stride_b,
+                   int64_t mask_stride_h, int64_t mask_ld, uint32_t *blocks, size_t blocks_words,
+                   void *stream);
 
 /*
  * fa_bwd_workspace_size -- bytes of device workspace that fa_bwd needs: two

@@ -29,8 +29,8 @@ def declared_functions():
 def test_exports_every_declared_function(fa_lib):
     names = declared_functions()
     assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_fwd", "fa_fwd_ext",
-                     "fa_fwd_fp8", "fa_fwd_gqa", "fa_paged_decode", "fa_paged_decode_workspace_size",
-                     "fa_quant_fp8", "fa_strerror"]
+                     "fa_fwd_fp8", "fa_fwd_gqa", "fa_mask_blocks", "fa_mask_blocks_words",
+                     "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_quant_fp8", "fa_strerror"]
     for n in names:
         assert hasattr(fa_lib, n), n
 
@@ -150,9 +150,9 @@ def test_bwd_workspace_size(fa_lib):
 
 
 def fext(lib, q=P, k=P, v=P, o=FAR[0], lse=FAR[1], B=1, H=2, Hkv=1, Nq=10, Nk=30, d=64,
-         scale=0.125, causal=1, wl=-1, wr=-1, mask=None, sb=0, sh=0, ldm=32, dtype=1):
+         scale=0.125, causal=1, wl=-1, wr=-1, mask=None, sb=0, sh=0, ldm=32, mb=None, dtype=1):
     return lib.fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, wl, wr, mask, sb, sh,
-                          ldm, dtype, None)
+                          ldm, mb, dtype, None)
 
 
 def test_fwd_ext_validation(fa_lib):
@@ -171,6 +171,42 @@ def test_fwd_ext_validation(fa_lib):
     assert fext(fa_lib, k=P + 4) == ALIGN
     assert fext(fa_lib, o=P) == INVALID                 # o overlaps q
     assert fext(fa_lib, o=FAR[2], mask=FAR[2] + 64) == INVALID  # o overlaps the mask
+    assert fext(fa_lib, mb=FAR[2]) == INVALID                   # a block map needs a mask
+    assert fext(fa_lib, mask=FAR[2], mb=FAR[3] + 2) == ALIGN
+    assert fext(fa_lib, mask=FAR[2], mb=FAR[0] + 16) == INVALID  # o overlaps the block map
+
+
+def mblocks(lib, mask=FAR[2], B=2, H=3, Nq=300, Nk=5000, sb=0, sh=0, ldm=5008, blocks=FAR[3],
+            words=1 << 20):
+    return lib.fa_mask_blocks(mask, B, H, Nq, Nk, sb, sh, ldm, blocks, words, None)
+
+
+def test_mask_blocks_words(fa_lib):
+    # ceil(300/128) = 3 query blocks, ceil(ceil(5000/64) / 32) = 3 words per half
+    assert fa.fa_mask_blocks_words(2, 3, 300, 5000, 0, 0) == 3 * 2 * 3
+    assert fa.fa_mask_blocks_words(2, 3, 300, 5000, 16, 0) == 2 * 3 * 2 * 3
+    assert fa.fa_mask_blocks_words(2, 3, 300, 5000, 16, 16) == 6 * 3 * 2 * 3
+    assert fa.fa_mask_blocks_words(1, 1, 128, 2048, 0, 0) == 2
+    assert fa.fa_mask_blocks_words(1, 1, 129, 2049, 0, 0) == 2 * 2 * 2
+    assert fa.fa_mask_blocks_words(0, 1, 10, 10, 0, 0) == 0
+    assert fa.fa_mask_blocks_words(1, 1, 10, 10, -16, 0) == 0
+
+
+def test_mask_blocks_validation(fa_lib):
+    assert mblocks(fa_lib, mask=0) == INVALID
+    assert mblocks(fa_lib, blocks=0) == INVALID
+    assert mblocks(fa_lib, Nq=0) == INVALID
+    assert mblocks(fa_lib, sb=-16) == INVALID
+    assert mblocks(fa_lib, ldm=4992) == INVALID                   # row stride below Nk
+    assert mblocks(fa_lib, words=17) == INVALID                   # 18 words needed
+    assert mblocks(fa_lib, Nq=1 << 16, Nk=1 << 16, ldm=1 << 16) == UNSUPPORTED  # slice >= 2^31
+    assert mblocks(fa_lib, ldm=5000) == ALIGN
+    assert mblocks(fa_lib, mask=FAR[2] + 8) == ALIGN
+    assert mblocks(fa_lib, blocks=FAR[3] + 2) == ALIGN
+    assert mblocks(fa_lib, blocks=FAR[2] + 5008) == INVALID       # the map overlaps the mask
+    # 2^16 * 2^16 slices of one query block and one word: a grid of 2^32 workgroups
+    assert mblocks(fa_lib, B=1 << 16, H=1 << 16, Nq=100, Nk=100, sb=1 << 20, sh=16, ldm=112,
+                   words=1 << 40) == UNSUPPORTED
 
 
 def quant(lib, x=P, dtype=1, B=1, H=2, N=100, d=128, layout=0, codes=FAR[0], exps=FAR[1]):

@@ -4,7 +4,13 @@ fp64 oracle, through the C ABI.
 Rows that see no key must come back as o = 0 and lse = -inf exactly; the
 others meet the forward's bar for their input type.  Full comparison on
 ragged shapes; at B=2 H=32 N=8192 d=128 (bf16) a causal sliding window and a
-broadcast boolean mask on 256 sampled rows per head.
+broadcast boolean mask on 256 sampled rows per head.  The mask's block map
+(fa_mask_blocks) must equal the oracle's bit for bit.  A forward given the map
+meets the same bar against the oracle, and stays within MAP_DIFF of the same
+forward without the map: the map only removes tiles that change nothing, but
+the tiles left over may run in the other of the loop body's two compiled
+copies (one per LDS buffer), which can round the reference's products in the
+last bit (observed: 2.4e-7 in O, two ulp in lse).
 """
 import numpy as np
 import pytest
@@ -18,6 +24,7 @@ from gpu_util import TOL, errors, progress
 pytestmark = pytest.mark.gpu
 
 DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+MAP_DIFF = 1e-5  # largest |difference| of o and of finite lse with and without the block map
 
 
 @pytest.fixture(autouse=True)
@@ -33,13 +40,26 @@ def ext_inputs(cid, B, H, Hkv, Nq, Nk, d, dtype):
     return q, k, v
 
 
-def check(q, k, v, causal, window, mask, dev, label, rows=None):
+def check(q, k, v, causal, window, mask, dev, label, rows=None, block_map=False):
     B, H, Nq, d = q.shape
     scale = float(np.float32(1.0 / np.sqrt(d)))
-    progress("fa_fwd_ext %s Nq=%d Nk=%d causal=%d window=%s mask=%s" % (
-        label, Nq, k.shape[2], causal, window, None if mask is None else tuple(mask.shape)))
-    o, lse = fa.forward_ext(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal,
-                            window=window, mask=None if mask is None else mask.to(dev))
+    progress("fa_fwd_ext %s Nq=%d Nk=%d causal=%d window=%s mask=%s map=%d" % (
+        label, Nq, k.shape[2], causal, window, None if mask is None else tuple(mask.shape),
+        block_map))
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    md = None if mask is None else mask.to(dev)
+    o, lse = fa.forward_ext(qd, kd, vd, scale=scale, causal=causal, window=window, mask=md,
+                            block_map=True if block_map else None)
+    if block_map:
+        o2, lse2 = fa.forward_ext(qd, kd, vd, scale=scale, causal=causal, window=window, mask=md)
+        torch.cuda.synchronize()
+        # the same rows see no key with and without the map
+        assert torch.equal(torch.isneginf(lse), torch.isneginf(lse2)), label
+        fin = torch.isfinite(lse2)
+        dmax = (o - o2).abs().max().item() if o.numel() else 0.0
+        lmax = (lse[fin] - lse2[fin]).abs().max().item() if fin.any() else 0.0
+        progress("%s map vs no map: max|dO|=%.3g max|dlse|=%.3g" % (label, dmax, lmax))
+        assert dmax <= MAP_DIFF and lmax <= MAP_DIFF, (label, dmax, lmax)
     torch.cuda.synchronize()
     ro, rl = oracle.attention_ext(q, k, v, scale, causal, window, mask, rows=rows)
     og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
@@ -127,3 +147,100 @@ def test_headline_boolean_mask_sampled(gpu, fa_lib):
     m[:, 0] = True
     rows = inputs.sample_rows(N, 256, seed=1000 * cfg.cid + 5)
     check(q, k, v, False, (-1, -1), m, gpu, "B2 H32 N8192 block-sparse mask", rows=rows)
+
+
+# ---- block map of the mask --------------------------------------------------
+
+def map_words(mp):
+    """uint32 view of a map tensor, shaped as the oracle's."""
+    return mp.cpu().numpy().view(np.uint32)
+
+
+MAP_CASES = [  # mask prefix, Nq, Nk, kind
+    ((), 1, 1, "ones"),
+    ((), 300, 5000, "sparse"),       # 79 key blocks over 3 words
+    ((), 129, 2049, "tril"),         # ragged query and key blocks
+    ((3,), 1000, 1000, "blocks"),    # per head
+    ((2, 1), 257, 700, "zeros"),     # per batch
+    ((2, 3), 640, 130, "dense"),     # per (b, h)
+]
+
+
+def make_mask(prefix, Nq, Nk, kind, seed):
+    g = np.random.default_rng(seed)
+    shape = prefix + (Nq, Nk)
+    if kind == "ones":
+        m = np.ones(shape, bool)
+    elif kind == "zeros":
+        m = np.zeros(shape, bool)
+    elif kind == "sparse":
+        m = g.random(shape) < 0.0005
+    elif kind == "tril":
+        m = np.broadcast_to(np.tril(np.ones((Nq, Nk), bool), Nk - Nq), shape).copy()
+    elif kind == "dense":
+        m = g.random(shape) < 0.999
+    else:  # "blocks": whole 128 x 64 blocks kept at random, then some single bytes flipped
+        keep = g.random(prefix + ((Nq + 127) // 128, (Nk + 63) // 64)) < 0.4
+        m = np.repeat(np.repeat(keep, 128, -2), 64, -1)[..., :Nq, :Nk].copy()
+        flip = g.random(shape) < 0.0002
+        m ^= flip
+    return torch.from_numpy(m)
+
+
+@pytest.mark.parametrize("prefix,Nq,Nk,kind", MAP_CASES)
+def test_mask_block_map_exact(gpu, fa_lib, prefix, Nq, Nk, kind):
+    m = make_mask(prefix, Nq, Nk, kind, 70 + Nq)
+    B, H = 2, 3
+    progress("fa_mask_blocks %s Nq=%d Nk=%d %s" % (prefix, Nq, Nk, kind))
+    mp = fa.mask_block_map(m.to(gpu), B, H, Nq, Nk)
+    torch.cuda.synchronize()
+    ref = oracle.mask_blocks(m)
+    assert mp.numel() == ref.size
+    assert (map_words(mp).reshape(ref.shape) == ref).all(), kind
+
+
+def test_mask_block_map_ignores_row_padding(gpu, fa_lib):
+    """Bytes between Nk and the row stride are not part of the mask."""
+    Nq, Nk, ldm = 200, 70, 96
+    m = make_mask((), Nq, Nk, "blocks", 75)
+    buf = torch.full((Nq, ldm), 255, dtype=torch.uint8)
+    buf[:, :Nk] = m.to(torch.uint8) * 3
+    bd = buf.to(gpu)
+    words = fa.fa_mask_blocks_words(1, 1, Nq, Nk, 0, 0)
+    mp = torch.full((words,), -1, dtype=torch.int32, device=gpu)
+    fa.fa_mask_blocks(bd, 1, 1, Nq, Nk, 0, 0, ldm, mp)
+    torch.cuda.synchronize()
+    ref = oracle.mask_blocks(m)
+    assert (map_words(mp).reshape(ref.shape) == ref).all()
+
+
+MAPPED = [  # dtype, prefix, Nq, Nk, causal, window, kind
+    ("bf16", (), 1000, 1000, True, (-1, -1), "blocks"),
+    ("f16", (4,), 333, 1200, False, (-1, -1), "blocks"),
+    ("f32", (), 700, 700, True, (-1, -1), "blocks"),          # 32-key tiles: two per block
+    ("bf16", (2, 1), 300, 5000, False, (-1, -1), "sparse"),   # long runs of empty blocks
+    ("bf16", (), 500, 2100, False, (300, 200), "blocks"),     # with a window
+    ("f32", (2, 4), 129, 2049, False, (-1, -1), "tril"),
+    ("bf16", (), 640, 640, False, (-1, -1), "zeros"),         # nothing visible
+    ("f16", (), 384, 384, False, (-1, -1), "ones"),           # everything visible
+]
+
+
+@pytest.mark.parametrize("dt,prefix,Nq,Nk,causal,window,kind", MAPPED)
+def test_boolean_masks_with_block_map(gpu, fa_lib, dt, prefix, Nq, Nk, causal, window, kind):
+    d = 64 if dt == "f32" else 128
+    q, k, v = ext_inputs(66, 2, 4, 2, Nq, Nk, d, DT[dt])
+    m = make_mask(prefix, Nq, Nk, kind, 80 + Nq)
+    check(q, k, v, causal, window, m, gpu, "%s map %s %s" % (dt, kind, prefix), block_map=True)
+
+
+def test_headline_block_sparse_mask_with_map_sampled(gpu, fa_lib):
+    cfg = inputs.FWD_CONFIGS[3]
+    q, k, v = inputs.fwd_inputs(cfg)
+    N = cfg.N
+    keep = torch.from_numpy(np.random.default_rng(64).random((N // 128, N // 64)) < 0.5)
+    m = keep.repeat_interleave(128, 0).repeat_interleave(64, 1) & torch.ones(N, N, dtype=torch.bool).tril()
+    m[:, 0] = True
+    rows = inputs.sample_rows(N, 256, seed=1000 * cfg.cid + 5)
+    check(q, k, v, False, (-1, -1), m, gpu, "B2 H32 N8192 block-sparse mask, map", rows=rows,
+          block_map=True)
