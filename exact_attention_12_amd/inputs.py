@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 __all__ = ["FwdConfig", "FWD_CONFIGS", "DecodeConfig", "DECODE_CONFIG", "normal",
-           "fwd_inputs", "bwd_dout", "sample_rows", "decode_inputs"]
+           "fwd_inputs", "bwd_dout", "sample_rows", "decode_inputs", "prefill_queries"]
 
 
 @dataclass(frozen=True)
@@ -136,6 +136,12 @@ DECODE_CONFIG = DecodeConfig()
 DECODE_GQA_CONFIG = DecodeConfig(cid=6, num_kv_heads=8,
                                  name="64 seqs, 32 query heads / 8 kv heads, head 128, fp16, block 16, "
                                       "ctx U[512,4096], 20000-block pool")
+
+
+def prefill_queries(cfg: DecodeConfig, Nq: int) -> torch.Tensor:
+    """Queries [S, H, Nq, D] of a chunked prefill over the cache of decode_inputs(cfg):
+    the last Nq tokens of each sequence's context, N(0,1) in cfg.dtype (CPU)."""
+    return normal(1000 * cfg.cid + 7, (cfg.num_seqs, cfg.num_heads, Nq, cfg.head_size), 1.0, cfg.dtype)
 
 
 def decode_inputs(cfg: DecodeConfig = DECODE_CONFIG, context_lens=None):

@@ -21,6 +21,7 @@ Functions (each cites the page passages it follows in ``oracle.c``):
                                                       gradients dQ, dK, dV
   e4m3_encode / e4m3_decode, quant_fp8, dequant_fp8  block-scaled FP8 (E4M3)
   paged_decode(...), paged_decode_partitioned(...)    single-query decode
+  paged_prefill(...)                                  Nq new queries over the paged cache
   widen(x)                                            exact fp64 view
 """
 import ctypes
@@ -78,6 +79,8 @@ def _load():
     lib.oracle_attention_ext.restype = i
     lib.oracle_mask_blocks.argtypes = [vp, i, i, i, i, i64, i64, i64, vp]
     lib.oracle_mask_blocks.restype = i
+    lib.oracle_paged_prefill.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, d, i, vp, vp, i]
+    lib.oracle_paged_prefill.restype = i
     lib.oracle_e4m3_encode.argtypes = [vp, i64, vp]
     lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
     lib.oracle_fp8_codes_len.argtypes = [i, i, i, i, i]
@@ -383,6 +386,27 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, nthread
                                      nthreads or default_threads())
     _check(st, "oracle_paged_decode")
     return out, lse
+
+
+def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, scale, causal, nthreads=None):
+    """Nq new queries per sequence (q [S, H, Nq, D], the last Nq tokens of each context)
+    over the paged cache, bottom-right causal or not: (o [S, H, Nq, D], lse [S, H, Nq]) fp64."""
+    qt, code = _host(q)
+    kt, c2 = _host(k_cache)
+    vt, c3 = _host(v_cache)
+    if not (code == c2 == c3):
+        raise ValueError("q and caches must share a dtype")
+    bt = np.ascontiguousarray(torch.as_tensor(block_tables).cpu().numpy().astype(np.int32))
+    cl = np.ascontiguousarray(torch.as_tensor(context_lens).cpu().numpy().astype(np.int32))
+    S, H, Nq, D = qt.shape
+    Hkv, BS = kt.shape[1], kt.shape[3]
+    o = np.empty((S, H, Nq, D), dtype=np.float64)
+    lse = np.empty((S, H, Nq), dtype=np.float64)
+    st = _load().oracle_paged_prefill(_p(qt), _p(kt), _p(vt), code, _p(bt), _p(cl), S, H, Hkv, Nq, D,
+                                      BS, bt.shape[1], float(scale), int(bool(causal)), _p(o), _p(lse),
+                                      nthreads or default_threads())
+    _check(st, "oracle_paged_prefill")
+    return o, lse
 
 
 def paged_decode_partitioned(q, k_cache, v_cache, block_tables, context_lens, scale, part_tokens,

@@ -1131,3 +1131,73 @@ int oracle_mask_blocks(const uint8_t *mask, int Bs, int Hs, int Nq, int Nk, int6
             }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Chunked prefill over the paged cache                                 */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Nq new query tokens per sequence attend to the sequence's context in the
+ * paged cache (the cache layouts of [PA] "Inputs", "Concepts", "Key",
+ * "Value"; one query token per sequence there, Nq here).  The queries are
+ * the context's last Nq tokens: query row i of sequence s is context token
+ * ctx_s - Nq + i, so the causal mask is aligned to the bottom-right corner
+ * ([YJ] 11.3's is_causal on a rectangle; reading 30).  Row i sees the
+ * context tokens t < ctx_s with (causal == 0 or t <= i + ctx_s - Nq), then
+ * the dense softmax over them ([SU] Eq. (1)); a row that sees no token gets
+ * O = 0 and lse = -inf.
+ *
+ * q [S, H, Nq, D]; caches as for the decode; o [S, H, Nq, D] and
+ * lse [S, H, Nq] fp64.
+ */
+typedef struct {
+    or_dec_ctx d;
+    int Nq, causal;
+    double *o, *lse;
+} or_pre_ctx;
+
+static void or_pre_item(void *vctx, int64_t item, double *scratch)
+{
+    const or_pre_ctx *x = (const or_pre_ctx *)vctx;
+    const or_dec_ctx *dx = &x->d;
+    int64_t i = item % x->Nq, sh = item / x->Nq;
+    int s = (int)(sh / dx->H), h = (int)(sh % dx->H);
+    int kvh = h / (dx->H / dx->Hkv);
+    int64_t ctx = dx->ctx_lens[s];
+    int64_t n = ctx;
+    if (x->causal) {
+        int64_t last = i + ctx - x->Nq; /* the row's own context position */
+        n = last + 1 < ctx ? last + 1 : ctx;
+        if (n < 0) n = 0;
+    }
+    int64_t qbase = item * dx->D;
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t blk = dx->bt[(int64_t)s * dx->MB + t / dx->BS];
+        int off = (int)(t % dx->BS);
+        double dot = 0.0;
+        for (int e = 0; e < dx->D; ++e)
+            dot += or_load(dx->q, dx->dtype, qbase + e) *
+                   or_load(dx->kc, dx->dtype, or_k_index(dx, blk, kvh, e, off));
+        scratch[t] = dx->scale * dot;
+    }
+    or_paged_v pv = { dx, s, kvh, 0 };
+    x->lse[item] = or_softmax_row(scratch, n, dx->D, or_paged_value, &pv, x->o + item * dx->D);
+}
+
+int oracle_paged_prefill(const void *q, const void *k_cache, const void *v_cache, int dtype,
+                         const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                         int num_heads, int num_kv_heads, int Nq, int head_size, int block_size,
+                         int max_blocks_per_seq, double scale, int causal, double *o, double *lse,
+                         int nthreads)
+{
+    if (or_dec_check(q, k_cache, v_cache, dtype, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_size, block_size, max_blocks_per_seq) || !o || !lse || Nq < 1)
+        return -1;
+    or_pre_ctx x = { { q, k_cache, v_cache, dtype, block_tables, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                       max_blocks_per_seq, 16 / or_elem_bytes(dtype), scale, 0,
+                       NULL, NULL, NULL, NULL, NULL, 0 },
+                     Nq, causal ? 1 : 0, o, lse };
+    int64_t maxctx = (int64_t)max_blocks_per_seq * block_size;
+    return or_parallel(or_pre_item, &x, (int64_t)num_seqs * num_heads * Nq, maxctx, nthreads);
+}

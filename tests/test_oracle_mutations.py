@@ -19,10 +19,22 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_decode.py",
               "tests/test_oracle_tiling.py", "tests/test_oracle_bwd.py", "tests/test_oracle_fp8.py",
-              "tests/test_oracle_ext.py", "tests/test_oracle_blocks.py"]
+              "tests/test_oracle_ext.py", "tests/test_oracle_blocks.py", "tests/test_oracle_prefill.py"]
 
 # (name, text in oracle.c, replacement); the text must occur in the source
 MUTATIONS = [
+    ("prefill_causal_offset_sign",
+     "int64_t last = i + ctx - x->Nq;",
+     "int64_t last = i - ctx + x->Nq;"),
+    ("prefill_causal_excludes_own_token",
+     "n = last + 1 < ctx ? last + 1 : ctx;",
+     "n = last < ctx ? last : ctx;"),
+    ("prefill_query_rows_collapsed",
+     "int64_t qbase = item * dx->D;",
+     "int64_t qbase = sh * dx->D;"),
+    ("prefill_kv_head_mapping",
+     "int kvh = h / (dx->H / dx->Hkv);",
+     "int kvh = h % dx->Hkv;"),
     ("mask_blocks_last_row_dropped",
      "for (int i = qb * 128; i < qb * 128 + 128 && i < Nq; ++i)",
      "for (int i = qb * 128; i < qb * 128 + 127 && i < Nq; ++i)"),
