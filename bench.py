@@ -18,7 +18,10 @@ One step = one pass of the whole path over one batch of synthetic input:
      keys (fwd_window) and with a block-sparse causal boolean mask
      (fwd_mask: each (128-query, 64-key) block kept with probability 1/2),
      and the same mask through its block map (fwd_mask_map: fa_mask_blocks
-     + fa_fwd_ext, the map rebuilt every step).
+     + fa_fwd_ext, the map rebuilt every step);
+  8. fa_fwd_paged, chunked prefill over the paged cache (fwd_paged): 16
+     sequences, 512 new tokens each at the end of a context of U[1024, 4096]
+     tokens, 32 query heads over 8 kv heads, bf16, block 16.
 Inputs are generated on the host with fixed seeds and copied to HBM before
 the timed region.  The timed region runs K steps between two device
 synchronisations; each kernel call is bracketed by HIP events recorded on the
@@ -187,6 +190,19 @@ def main():
                       device=dev)
     del gdec["k_cache"], gdec["v_cache"]
 
+    pcfg = inputs.PREFILL_CONFIG
+    log("generating chunked-prefill inputs: " + pcfg.name)
+    pdec = inputs.decode_inputs(pcfg)
+    pq = inputs.prefill_queries(pcfg, inputs.PREFILL_NQ).to(dev)
+    pk, pv = pdec["k_cache"].to(dev), pdec["v_cache"].to(dev)
+    pbt, pcl = pdec["block_tables"].to(dev), pdec["context_lens"].to(dev)
+    pctx = pdec["context_lens"].numpy().astype(np.int64)
+    pS, pH, pNq, pD = pq.shape
+    pHkv, pNB = pk.shape[1], pk.shape[0]
+    po = torch.empty((pS, pH, pNq, pD), dtype=torch.float32, device=dev)
+    pl = torch.empty((pS, pH, pNq), dtype=torch.float32, device=dev)
+    del pdec["k_cache"], pdec["v_cache"]
+
     log("generating the upstream gradient of the backward pass")
     gdo = inputs.bwd_dout(fcfg).to(dev)
     bdq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
@@ -264,13 +280,17 @@ def main():
                       mask_blocks=mask_map, stream=stream)
         if evs:
             evs[11].record(stream)
+        fa.fa_fwd_paged(pq, pk, pv, pbt, pcl, po, pl, pS, pH, pHkv, pNq, pD, 16, pNB, pbt.shape[1],
+                        float(np.float32(pcfg.scale)), True, stream=stream)
+        if evs:
+            evs[12].record(stream)
 
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(13)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -316,12 +336,18 @@ def main():
     mkb_tf = mk_flops / (mkb_avg * 1e-3) / 1e12
     mkb_all_tf = mk_flops / ((map_avg + mkb_avg) * 1e-3) / 1e12
     map_gbs = N * N / (map_avg * 1e-3) / 1e9  # the mask's bytes, read once
+    pg_ms = [e[11].elapsed_time(e[12]) for e in evs]
+    pg_avg = sum(pg_ms) / len(pg_ms)
+    # visible pairs: row i of a context of c tokens sees min(i + c - Nq + 1, c) of them
+    pg_pairs = sum(int(np.clip(np.arange(pNq) + c - pNq + 1, 0, c).sum()) for c in pctx)
+    pg_flops = 4.0 * pH * pD * pg_pairs
+    pg_tf = pg_flops / (pg_avg * 1e-3) / 1e12
 
     # quick sanity of the last step's results (full parity lives in the tests)
     finite = bool(torch.isfinite(o).all().item() and torch.isfinite(dout).all().item()
                   and torch.isfinite(gout).all().item() and torch.isfinite(go).all().item()
                   and all(torch.isfinite(t).all().item() for t in (bdq, bdk, bdv, o8, ow, om))
-                  and (om - omb).abs().max().item() <= 1e-5)
+                  and (om - omb).abs().max().item() <= 1e-5 and torch.isfinite(po).all().item())
 
     flops = fcfg.flops()
     tflops = flops / (fwd_avg * 1e-3) / 1e12
@@ -450,6 +476,15 @@ def main():
                                       "frac": round(mkb_tf / PEAK_BF16_TFLOPS, 4),
                                       "kernel": "fa_fwd_kernel<bf16,128,ext+mask> with the map",
                                       "algorithmic_per_launch": mk_flops}},
+        "fwd_paged": {"metric": "chunked prefill over the paged cache, TFLOP/s over visible pairs",
+                      "value": round(pg_tf, 2), "unit": "TFLOP/s", "workload": pcfg.name,
+                      "new_tokens_per_seq": pNq, "sum_ctx": int(pctx.sum()),
+                      "kernel_ms_avg": round(pg_avg, 4),
+                      "roofline": {"bound": "mfma", "achieved": round(pg_tf, 2),
+                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": round(pg_tf / PEAK_BF16_TFLOPS, 4),
+                                   "kernel": "fa_fwd_kernel<bf16,128,ext paged>",
+                                   "algorithmic_per_launch": pg_flops}},
         "decode_gqa": {"metric": "paged decode HBM bandwidth, 4 query heads per kv head",
                        "value": round(gqa_gbs, 1), "unit": "GB/s",
                        "workload": gcfg.name, "sum_ctx": int(gctx.sum()),

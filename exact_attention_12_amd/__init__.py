@@ -24,7 +24,7 @@ __all__ = [
     "fa_fwd_fp8", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror", "forward",
     "backward", "quant_fp8", "forward_fp8", "paged_decode", "lib_path", "load_library",
     "FA_FP8_BLOCK_ROWS", "FA_MASK_BLOCK_ROWS", "FA_MASK_BLOCK_COLS", "fa_mask_blocks_words",
-    "fa_mask_blocks", "mask_block_map",
+    "fa_mask_blocks", "mask_block_map", "fa_fwd_paged", "forward_paged",
 ]
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
@@ -74,6 +74,8 @@ def load_library():
     lib.fa_mask_blocks_words.restype = sz
     lib.fa_mask_blocks.argtypes = [vp, i, i, i, i, i64, i64, i64, vp, sz, vp]
     lib.fa_mask_blocks.restype = i
+    lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_paged.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -165,6 +167,21 @@ def fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window_left
                                    int(dtype), _stream(stream))
     if st != 0:
         raise FAError(st, "fa_fwd_ext")
+
+
+def fa_fwd_paged(q, k_cache, v_cache, block_tables, context_lens, o, lse, num_seqs, num_heads,
+                 num_kv_heads, Nq, head_size, block_size, num_blocks, max_blocks_per_seq, scale,
+                 causal, dtype=None, stream=None):
+    """C entry point ``fa_fwd_paged``: Nq new queries per sequence over the paged cache."""
+    if dtype is None:
+        dtype = _dtype_code(q.dtype)
+    st = load_library().fa_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                     _ptr(context_lens), _ptr(o), _ptr(lse), int(num_seqs),
+                                     int(num_heads), int(num_kv_heads), int(Nq), int(head_size),
+                                     int(block_size), int(num_blocks), int(max_blocks_per_seq),
+                                     float(scale), int(bool(causal)), int(dtype), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_fwd_paged")
 
 
 def fa_mask_blocks_words(B, H, Nq, Nk, mask_stride_b, mask_stride_h) -> int:
@@ -356,6 +373,28 @@ def forward_ext(q, k, v, scale=None, causal=False, window=(-1, -1), mask=None, b
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window[0], window[1], mask,
                sb, sh, ldm, mask_blocks=blocks, stream=stream)
+    return o, lse
+
+
+def forward_paged(q, k_cache, v_cache, block_tables, context_lens, scale=None, causal=True,
+                  stream=None):
+    """Allocate o, lse and run ``fa_fwd_paged``: q [S, H, Nq, D] (the last Nq tokens of
+    each context), caches as for ``paged_decode``; returns (o, lse)."""
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("block_tables", block_tables, torch.int32)
+    _check_dev("context_lens", context_lens, torch.int32)
+    if q.dim() != 4 or k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("q must be [S, H, Nq, D], k_cache [blocks, Hkv, D/x, BS, x], "
+                         "v_cache [blocks, Hkv, D, BS]")
+    S, H, Nq, D = q.shape
+    NB, Hkv, BS = k_cache.shape[0], k_cache.shape[1], k_cache.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty((S, H, Nq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((S, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_paged(q, k_cache, v_cache, block_tables, context_lens, o, lse, S, H, Hkv, Nq, D, BS, NB,
+                 block_tables.shape[1], scale, causal, stream=stream)
     return o, lse
 
 

@@ -29,6 +29,10 @@ hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *
                             int wr, const uint8_t *mask, int64_t msb, int64_t msh, int ldm,
                             const uint32_t *blocks, int dtype, hipStream_t stream);
 size_t mask_blocks_words(int B, int H, int Nq, int Nk, int64_t msb, int64_t msh);
+hipError_t fwd_paged_dispatch(const void *q, const void *kc, const void *vc, const int32_t *tables,
+                              const int32_t *ctx_lens, float *o, float *lse, int S, int H, int Hkv,
+                              int Nq, int mbps, uint64_t cache_bytes, float scale, int causal,
+                              int dtype, hipStream_t stream);
 hipError_t mask_blocks_dispatch(const uint8_t *mask, int B, int H, int Nq, int Nk, int64_t msb,
                                 int64_t msh, int ldm, uint32_t *blocks, hipStream_t stream);
 hipError_t quant_fp8_dispatch(const void *x, int dtype, int B, int H, int N, int d, int layout,
@@ -198,6 +202,47 @@ extern "C" int fa_fwd_ext(const void *q, const void *k, const void *v, float *o,
         fa::fwd_ext_dispatch(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, window_left,
                              window_right, mask, mask_stride_b, mask_stride_h, (int)mask_ld,
                              mask_blocks, dtype, (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens, float *o,
+                            float *lse, int num_seqs, int num_heads, int num_kv_heads, int Nq,
+                            int head_size, int block_size, int num_blocks, int max_blocks_per_seq,
+                            float scale, int causal, int dtype, void *stream)
+{
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !o || !lse)
+        return FA_ERR_INVALID_ARG;
+    if (num_seqs < 1 || num_heads < 1 || num_kv_heads < 1 || Nq < 1 || head_size < 1 ||
+        block_size < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
+        return FA_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return FA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+    const int es = elem_bytes(dtype);
+    if (es == 0) return FA_ERR_INVALID_ARG;
+    if (dtype == FA_F32 || head_size != 128 || block_size != 16) return FA_ERR_UNSUPPORTED;
+    const uint64_t cache_bytes = (uint64_t)num_blocks * num_kv_heads * head_size * block_size * es;
+    if (cache_bytes >= (1ull << 32)) return FA_ERR_UNSUPPORTED;  // 32-bit buffer offsets
+    if ((int64_t)Nq + 16 * (int64_t)max_blocks_per_seq >= (1 << 29)) return FA_ERR_UNSUPPORTED;
+    const int64_t qtiles = ((int64_t)Nq + kFwdRowsPerWorkgroup - 1) / kFwdRowsPerWorkgroup;
+    if ((int64_t)num_seqs * num_heads * qtiles > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)num_seqs * max_blocks_per_seq > INT_MAX) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return FA_ERR_ALIGNMENT;
+    const uint64_t rows = (uint64_t)num_seqs * num_heads * Nq;
+    const uint64_t o_bytes = rows * head_size * 4, l_bytes = rows * 4;
+    if (overlap(o, o_bytes, lse, l_bytes)) return FA_ERR_INVALID_ARG;
+    const void *ins[5] = {q, k_cache, v_cache, block_tables, context_lens};
+    const uint64_t in_bytes[5] = {rows * head_size * es, cache_bytes, cache_bytes,
+                                  (uint64_t)num_seqs * max_blocks_per_seq * 4, (uint64_t)num_seqs * 4};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(o, o_bytes, ins[i], in_bytes[i]) || overlap(lse, l_bytes, ins[i], in_bytes[i]))
+            return FA_ERR_INVALID_ARG;
+    const hipError_t e = fa::fwd_paged_dispatch(q, k_cache, v_cache, block_tables, context_lens, o, lse,
+                                                num_seqs, num_heads, num_kv_heads, Nq, max_blocks_per_seq,
+                                                cache_bytes, scale, causal ? 1 : 0, dtype,
+                                                (hipStream_t)stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -85,11 +85,19 @@ struct FwdExt {
     const uint32_t *blocks;
     int nkw;              // words per half of a query block's entry
     int64_t bmb, bmh;     // word strides of the map between batches and heads
+    // Paged K/V (EXT 4): K and V are the caches [blocks, Hkv, D/8, 16, 8] and
+    // [blocks, Hkv, D, 16]; sequence b's keys are its context_lens[b] context
+    // tokens, token t in block tables[b * mbps + t / 16] at slot t % 16.
+    const int32_t *tables, *ctx_lens;
+    int mbps;               // block-table entries per sequence
+    uint32_t cache_bytes;   // bytes of one cache (< 4 GiB)
 };
 
 // EXT: 0 = square path (N queries and keys, optional top-left causal mask),
 // 1 = general ranges (rectangular / windowed / bottom-right causal), 2 = 1
-// plus a boolean mask, 3 = 2 with the mask's block map.
+// plus a boolean mask, 3 = 2 with the mask's block map, 4 = 1 with K/V read
+// from the paged cache (the number of keys and the diagonal's offset come
+// from each sequence's context length).
 template <typename T, int D, bool CAUSAL, int EXT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(FwdCfg<T, D>::WPE, FwdCfg<T, D>::WPE)))
@@ -98,8 +106,10 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                    float scale, int H, int group, FwdExt ext)
 {
     static_assert(EXT == 0 || !CAUSAL, "general masks fold causality into the window");
-    const int NK = EXT ? ext.Nk : N;  // keys
     using C = FwdCfg<T, D>;
+    constexpr bool HAS_MASK = EXT == 2 || EXT == 3;  // a boolean mask rides along
+    static_assert(EXT != 4 || (C::ES == 2 && D == 128 && C::BC == 64 && C::NLD_W == 4),
+                  "paged K/V: each wave loads one 16-token cache block of K and of V per tile");
     static_assert(C::BR == 128 && 64 % C::BC == 0, "a block of the mask's map (128 x 64) is whole tiles");
     using M = Mma<T>;
     using frag = typename M::frag;
@@ -107,8 +117,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // boolean mask: a (BR x BC)-byte tile of it rides along with each K/V tile,
     // rows of BC bytes with the 16-byte chunks swizzled by swzm()
     constexpr int MCPR = C::BC / 16;                            // 16-byte chunks per mask row
-    constexpr int MASKB = EXT >= 2 ? C::BR * C::BC : 0;         // mask tile bytes
-    constexpr int NLDM_W = EXT >= 2 ? C::BR * MCPR / kWave / 4 : 0;  // its 1 KiB loads per wave
+    constexpr int MASKB = HAS_MASK ? C::BR * C::BC : 0;         // mask tile bytes
+    constexpr int NLDM_W = HAS_MASK ? C::BR * MCPR / kWave / 4 : 0;  // its 1 KiB loads per wave
     constexpr int SB = C::STAGEB + MASKB;                        // bytes per stage
     auto swzm = [](int row) { return MCPR == 4 ? (row >> 2) & 3 : (row >> 3) & 1; };
     __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
@@ -133,10 +143,19 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     const int bh = wid / wg_per_head;
     const int pi = wid % wg_per_head;
 
+    // keys of this head and the diagonal's offset (paged: per sequence)
+    int NK = EXT ? ext.Nk : N;
+    int OFF = ext.off;
+    if constexpr (EXT == 4) {
+        NK = ext.ctx_lens[bh / H];
+        OFF = NK - N;
+    }
+
     // Q, O, lse: head bh = b*H + h.  K, V: kv head b*(H/group) + h/group
     // (group query heads share one kv head; group = 1 is multi-head attention).
     const int64_t head = (int64_t)bh * N * D;
-    const int64_t kv_head = ((int64_t)(bh / H) * (H / group) + (bh % H) / group) * NK * D;
+    const int kvh = (bh % H) / group;  // paged: the kv head inside a cache block
+    const int64_t kv_head = EXT == 4 ? 0 : ((int64_t)(bh / H) * (H / group) + kvh) * NK * D;
     const T *Qh = Q + head;
     const T *Kh = K + kv_head;
     const T *Vh = V + kv_head;
@@ -162,13 +181,13 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         ld_row[i] = q / C::CPR;
         ld_off[i] = (ld_row[i] * D + ((q % C::CPR) ^ swz<C::CPR, C::ES>(ld_row[i])) * C::VEC) * C::ES;
     }
-    const int head_bytes = NK * C::ROWB;
+    const int head_bytes = EXT == 4 ? (int)ext.cache_bytes : NK * C::ROWB;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)Kh, 0, head_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)Vh, 0, head_bytes, kBufferFlags);
     const uint8_t *mbase = nullptr;
-    if constexpr (EXT >= 2) mbase = ext.mask + (int64_t)(bh / H) * ext.msb + (int64_t)(bh % H) * ext.msh;
+    if constexpr (HAS_MASK) mbase = ext.mask + (int64_t)(bh / H) * ext.msb + (int64_t)(bh % H) * ext.msh;
     const __amdgpu_buffer_rsrc_t mrs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)mbase, 0, EXT >= 2 ? N * ext.ldm : 0, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void *)mbase, 0, HAS_MASK ? N * ext.ldm : 0, kBufferFlags);
     // per-lane mask-tile load offsets (set per query tile): load I, lane l
     // fills chunk position p = I*64 + l = row p / MCPR, position p % MCPR
     // holding chunk (p % MCPR) ^ swzm(row) of mask row q0 + row
@@ -181,10 +200,47 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             m_off[i] = (q0_ + row) * ext.ldm + ((p % MCPR) ^ swzm(row)) * 16;
         }
     };
+    // Paged K/V: wave w loads cache block 4j + w of tile j (its 16 keys).
+    // K keeps the layout above: LDS chunk position q of the wave's loads
+    // holds chunk (q % CPR) ^ swz(row) of token row % 16, which the cache
+    // block holds at byte ((chunk * 16) + row % 16) * 16.  V is copied block
+    // by block as the cache holds it, [d][16 tokens] (4 KiB per block), with
+    // the two 16-byte halves of a d-row swapped for d & 8 (bank spread for
+    // the operand reads below).  The block id, a scalar load from the table
+    // row (which stays in the scalar cache across consecutive tiles), is the
+    // load's scalar offset.  Blocks past the context re-read its last block:
+    // their keys are masked and their values are zeroed before use.
+    int kp_off[EXT == 4 ? C::NLD_W : 1], vp_off[EXT == 4 ? C::NLD_W : 1];
+    const int32_t *trow = nullptr;  // this sequence's block-table row
+    int last_blk = 0;
+    if constexpr (EXT == 4) {
+#pragma unroll
+        for (int i = 0; i < C::NLD_W; ++i) {
+            const int q = (wave * C::NLD_W + i) * kWave + lane;
+            const int row = q / C::CPR;
+            kp_off[i] = (((q % C::CPR) ^ swz<C::CPR, C::ES>(row)) * 16 + row % 16) * 16;
+            const int p = i * kWave + lane, d = p / 2;
+            vp_off[i] = (d * 2 + ((p % 2) ^ ((d >> 3) & 1))) * 16;
+        }
+        trow = ext.tables + (int64_t)(bh / H) * ext.mbps;
+        last_blk = min(max(NK - 1, 0) / 16, ext.mbps - 1);
+    }
     auto load_tile = [&](int j, int buf, bool with_mask) {
         const int k0 = j * C::BC;
         char *kd = smem + buf * SB;
         char *vd = kd + C::TILEB;
+        if constexpr (EXT == 4) {
+            const uint32_t blk = (uint32_t)trow[min(j * 4 + wave, last_blk)];
+            // (block, kv head) slab of 4 KiB; below 4 GiB (checked by the host)
+            const int boff = (int)((blk * (uint32_t)(H / group) + (uint32_t)kvh) * (uint32_t)(D * 16 * C::ES));
+#pragma unroll
+            for (int i = 0; i < C::NLD_W; ++i) {
+                const int I = wave * C::NLD_W + i;
+                buffer_load_lds16(krs, kd + I * 1024, kp_off[i], boff);
+                buffer_load_lds16(vrs, vd + I * 1024, vp_off[i], boff);
+            }
+            return;
+        }
         const int soff = k0 * C::ROWB;
         if (k0 + C::BC <= NK) {
 #pragma unroll
@@ -204,7 +260,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                 buffer_load_lds16(vrs, vd + I * 1024, off, soff);
             }
         }
-        if constexpr (EXT >= 2) {
+        if constexpr (HAS_MASK) {
             // rows past the end of the mask read as 0 (buffer bounds)
             if (with_mask) {
 #pragma unroll
@@ -248,7 +304,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // K operands are read from LDS in groups of two steps, one group
     // ahead of the matrix products that use them.
     auto qk = [&](const char *Ks, f32x16 (&s)[C::NKB]) {
-        constexpr int G = EXT >= 2 ? 1 : 2;  // registers for the boolean mask
+        constexpr int G = HAS_MASK ? 1 : 2;  // registers for the boolean mask
         constexpr int NG = C::QK_STEPS / G;
         frag kf[2][G][C::NKB];
         auto rd = [&](int g, int b) {
@@ -282,8 +338,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         int first = 0;
         if constexpr (EXT != 0) {
             const int qr = min(qrow, N - 1);  // rows past the end behave like row N-1
-            last = min(qr + ext.off + ext.wr, NK - 1);
-            first = qr + ext.off - ext.wl;
+            last = min(qr + OFF + ext.wr, NK - 1);
+            first = qr + OFF - ext.wl;
         }
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
@@ -313,7 +369,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             for (int r = 0; r < 16; ++r) {
                 bool off_ = acc_row(r, 0) > lim[kb];
                 if constexpr (EXT != 0) off_ = off_ || acc_row(r, 0) < lo[kb];
-                if constexpr (EXT >= 2) off_ = off_ || ((mw[kb][r / 4] >> (8 * (r % 4))) & 0xffu) == 0;
+                if constexpr (HAS_MASK) off_ = off_ || ((mw[kb][r / 4] >> (8 * (r % 4))) & 0xffu) == 0;
                 if (off_) s[kb][r] = -INFINITY;
                 else bits |= 1u << (kb * 16 + r);
             }
@@ -372,7 +428,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         const int k0 = j * C::BC;
         if (jn < ntiles) load_tile(jn, STAGE ^ 1, part_n);
         uint32_t mcur[C::NKB][4];
-        if constexpr (EXT >= 2) {
+        if constexpr (HAS_MASK) {
             if (part) {
                 read_mask(smem + STAGE * SB + C::STAGEB, mcur);
             } else {
@@ -389,7 +445,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         const char *Vs = Ks + C::TILEB;
 
         bool skip = EXT != 0 && (j < jw_beg || j >= jw_end);  // no row of the wave sees a key here
-        if constexpr (EXT >= 2) {
+        if constexpr (HAS_MASK) {
             // ... or the mask hides every key of the tile from every row of the wave
             if (part) {
                 uint32_t any = 0;
@@ -409,9 +465,9 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         qk(Ks, s);
         bool need_mask = (k0 + C::BC > NK) || (CAUSAL && k0 + C::BC - 1 > wq_lo);
         if constexpr (EXT != 0)
-            need_mask = k0 < min(wq_hi, N - 1) + ext.off - ext.wl ||
-                        k0 + C::BC - 1 > min(wq_lo + ext.off + ext.wr, NK - 1);
-        if constexpr (EXT >= 2) need_mask = need_mask || part || wq_hi >= N;
+            need_mask = k0 < min(wq_hi, N - 1) + OFF - ext.wl ||
+                        k0 + C::BC - 1 > min(wq_lo + OFF + ext.wr, NK - 1);
+        if constexpr (HAS_MASK) need_mask = need_mask || part || wq_hi >= N;
         int lim[C::NKB], lo[C::NKB];
         limits(k0, lim, lo);
         uint32_t vis = 0;
@@ -432,13 +488,13 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         // part in that decision (their mc_ref starts at 0, so that their
         // probabilities come out as exp2(-inf) = 0 without a reference).
         if (EXT == 0 ? j == 0
-                     : __builtin_amdgcn_ballot_w64(m_ref == -INFINITY && (EXT < 2 || qrow < N)) != 0)
+                     : __builtin_amdgcn_ballot_w64(m_ref == -INFINITY && (!HAS_MASK || qrow < N)) != 0)
             rebase(s);
         float rs = exponentiate(s);
         if ((EXT != 0 || j != 0) && __builtin_amdgcn_ballot_w64(!(rs <= kPMax)) != 0) {
             qk(Ks, s);
             if (need_mask) {
-                if constexpr (EXT >= 2) apply_bits(s, vis);
+                if constexpr (HAS_MASK) apply_bits(s, vis);
                 else apply_mask(s, lim, lo, mcur);
             }
             rebase(s);
@@ -462,7 +518,25 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
                     frag a;
-                    if constexpr (C::ES == 2) {
+                    if constexpr (EXT == 4) {
+                        // Paged V, [d][16 tokens] per 4 KiB block: block 2kb+st of
+                        // the tile holds keys kb*32 + 16*st + 0..15; this lane takes
+                        // tokens 4h..4h+3 and 8+4h..8+4h+3 of head element d.
+                        const int dd = db * 32 + col, sw = (dd >> 3) & 1;
+                        const char *vb = Vs + (2 * kb + st) * 4096 + dd * 32 + 8 * h;
+                        s16x4 lo = *(const s16x4 *)(vb + 16 * sw);
+                        s16x4 hi = *(const s16x4 *)(vb + 16 * (sw ^ 1));
+                        if (k0 + C::BC > NK) {
+                            // slots past the context may hold anything: 0 * V must be 0
+                            const int t0 = k0 + (2 * kb + st) * 16 + 4 * h;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if (t0 + e >= NK) lo[e] = 0;
+                                if (t0 + 8 + e >= NK) hi[e] = 0;
+                            }
+                        }
+                        a = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    } else if constexpr (C::ES == 2) {
                         // Two transpose reads, each giving this lane 4
                         // consecutive keys of head element db*32 + col: keys
                         // kb*32 + 16*st + 4*h (+8) + 0..3.  Source lane r of
@@ -514,21 +588,21 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         // keys [kbeg, kend) can be seen by the workgroup's rows, and
         // [kw_beg, kw_end) by this wave's
         const int q_last = min(q0 + C::BR, N) - 1;
-        const int kbeg = max(0, q0 + ext.off - ext.wl);
-        kend = min(NK, q_last + ext.off + ext.wr + 1);
+        const int kbeg = max(0, q0 + OFF - ext.wl);
+        kend = min(NK, q_last + OFF + ext.wr + 1);
         jbeg = kbeg / C::BC;
         const int w_last = min(wq_hi, N - 1);
-        const int kw_beg = max(0, wq_lo + ext.off - ext.wl);
-        const int kw_end = min(NK, w_last + ext.off + ext.wr + 1);
+        const int kw_beg = max(0, wq_lo + OFF - ext.wl);
+        const int kw_end = min(NK, w_last + OFF + ext.wr + 1);
         jw_beg = kw_beg / C::BC;
         jw_end = (wq_lo < N && kw_end > kw_beg) ? (kw_end + C::BC - 1) / C::BC : 0;
-        if constexpr (EXT >= 2) set_mask_offsets(q0);
+        if constexpr (HAS_MASK) set_mask_offsets(q0);
     }
     ntiles = kend > jbeg * C::BC ? (kend + C::BC - 1) / C::BC : jbeg;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
     m_ref = -INFINITY;
-    mc_ref = EXT >= 2 ? 0.f : -INFINITY;
+    mc_ref = HAS_MASK ? 0.f : -INFINITY;
     l_run = 0.f;
     l_hat = 0.f;
 
@@ -837,6 +911,30 @@ hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *
         return d == 64 ? launch_fwd_ext<_Float16, 64>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream)
                        : launch_fwd_ext<_Float16, 128>(q, k, v, o, lse, B, H, Hkv, Nq, scale, ext, stream);
     }
+}
+
+// Chunked prefill over the paged cache (EXT 4).  Arguments validated by the
+// caller: dtype 1/2, head size 128, block size 16, one cache below 4 GiB,
+// Nq + 16 * mbps < 2^29.
+hipError_t fwd_paged_dispatch(const void *q, const void *kc, const void *vc, const int32_t *tables,
+                              const int32_t *ctx_lens, float *o, float *lse, int S, int H, int Hkv,
+                              int Nq, int mbps, uint64_t cache_bytes, float scale, int causal,
+                              int dtype, hipStream_t stream)
+{
+    const int big = Nq + 16 * mbps;  // beyond every row's reach: unbounded
+    const FwdExt ext{0, 0, big, causal ? 0 : big, nullptr, 0, 0, 0, nullptr, 0, 0, 0,
+                     tables, ctx_lens, mbps, (uint32_t)cache_bytes};
+    const int nqt = (Nq + 127) / 128;
+    const dim3 grid((unsigned)((int64_t)S * H * nqt));
+    if (dtype == 2)
+        hipLaunchKernelGGL((fa_fwd_kernel<_Float16, 128, false, 4>), grid, dim3(256), 0, stream,
+                           (const _Float16 *)q, (const _Float16 *)kc, (const _Float16 *)vc, o, lse, Nq, nqt,
+                           scale, H, H / Hkv, ext);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<__bf16, 128, false, 4>), grid, dim3(256), 0, stream,
+                           (const __bf16 *)q, (const __bf16 *)kc, (const __bf16 *)vc, o, lse, Nq, nqt, scale,
+                           H, H / Hkv, ext);
+    return hipGetLastError();
 }
 
 }  // namespace fa

@@ -19,7 +19,8 @@ import numpy as np
 import torch
 
 __all__ = ["FwdConfig", "FWD_CONFIGS", "DecodeConfig", "DECODE_CONFIG", "normal",
-           "fwd_inputs", "bwd_dout", "sample_rows", "decode_inputs", "prefill_queries"]
+           "fwd_inputs", "bwd_dout", "sample_rows", "decode_inputs", "prefill_queries",
+           "PREFILL_CONFIG", "PREFILL_NQ"]
 
 
 @dataclass(frozen=True)
@@ -136,6 +137,15 @@ DECODE_CONFIG = DecodeConfig()
 DECODE_GQA_CONFIG = DecodeConfig(cid=6, num_kv_heads=8,
                                  name="64 seqs, 32 query heads / 8 kv heads, head 128, fp16, block 16, "
                                       "ctx U[512,4096], 20000-block pool")
+
+
+# chunked prefill over the paged cache: 16 sequences, 512 new tokens each at
+# the end of a context of U[1024, 4096] tokens, 32 query heads over 8 kv heads
+PREFILL_CONFIG = DecodeConfig(cid=10, num_seqs=16, num_heads=32, num_kv_heads=8, ctx_lo=1024,
+                              ctx_hi=4096, dtype=torch.bfloat16,
+                              name="16 seqs x 512 new tokens, 32 query heads / 8 kv heads, head 128, "
+                                   "bf16, block 16, ctx U[1024,4096], 20000-block pool")
+PREFILL_NQ = 512
 
 
 def prefill_queries(cfg: DecodeConfig, Nq: int) -> torch.Tensor:

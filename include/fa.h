@@ -153,6 +153,45 @@ int fa_fwd_ext(const void *q, const void *k, const void *v, float *o, float *lse
                int64_t mask_ld, const uint32_t *mask_blocks, int dtype, void *stream);
 
 /*
+ * fa_fwd_paged -- chunked prefill over the paged KV cache: Nq new query
+ * tokens per sequence attend to the sequence's context, read in place from
+ * the cache of fa_paged_decode (the layouts of the PagedAttention
+ * walkthrough, data-sketchers.com wiki, sections "Inputs" and "Concepts").
+ * The queries are the context's last Nq tokens, so the causal mask is
+ * aligned to the bottom-right corner (youngju.dev section 11.3, is_causal):
+ * query row i of sequence s sees the context tokens
+ *     t < ctx_s   and   (causal == 0 or t <= i + ctx_s - Nq),
+ * with ctx_s = context_lens[s]; a row that sees no token gets o = 0 and
+ * lse = -inf.
+ *
+ *   q            : [num_seqs, num_heads, Nq, head_size], 16-byte aligned.
+ *   k_cache      : [num_blocks, num_kv_heads, head_size/8, block_size, 8].
+ *   v_cache      : [num_blocks, num_kv_heads, head_size, block_size].
+ *                  Both 16-byte aligned; one cache must stay below 4 GiB.
+ *   block_tables : [num_seqs, max_blocks_per_seq] int32; token t of sequence
+ *                  s is in block block_tables[s][t / block_size], slot
+ *                  t % block_size.
+ *   context_lens : [num_seqs] int32, device.  Not validated on the device:
+ *                  each must lie in [0, block_size * max_blocks_per_seq] and
+ *                  every table entry below ceil(ctx_s / block_size) in
+ *                  [0, num_blocks).  A length or entry outside that gives
+ *                  wrong results but reads nothing outside the caches,
+ *                  tables and lengths.
+ *   o            : [num_seqs, num_heads, Nq, head_size] fp32;  lse :
+ *                  [num_seqs, num_heads, Nq] fp32 (natural log), as fa_fwd.
+ *   head_size 128, block_size 16, dtype FA_BF16 or FA_F16 (q and both
+ *   caches), num_kv_heads dividing num_heads (query head h reads kv head
+ *   h / (num_heads / num_kv_heads)); else FA_ERR_UNSUPPORTED /
+ *   FA_ERR_INVALID_ARG.  Products and accumulation as fa_fwd.
+ *   FA_ERR_UNSUPPORTED also when Nq + 16 * max_blocks_per_seq >= 2^29.
+ * o and lse must not overlap any input or each other; stream as fa_fwd.
+ */
+int fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                 const int32_t *context_lens, float *o, float *lse, int num_seqs, int num_heads,
+                 int num_kv_heads, int Nq, int head_size, int block_size, int num_blocks,
+                 int max_blocks_per_seq, float scale, int causal, int dtype, void *stream);
+
+/*
  * Block map of a boolean mask, for fa_fwd_ext: which blocks of
  * FA_MASK_BLOCK_ROWS query rows x FA_MASK_BLOCK_COLS keys hold a visible
  * pair, and which hold no masked one.  The map is this library's own

@@ -29,7 +29,7 @@ def declared_functions():
 def test_exports_every_declared_function(fa_lib):
     names = declared_functions()
     assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fp8_codes_bytes", "fa_fwd", "fa_fwd_ext",
-                     "fa_fwd_fp8", "fa_fwd_gqa", "fa_mask_blocks", "fa_mask_blocks_words",
+                     "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_paged", "fa_mask_blocks", "fa_mask_blocks_words",
                      "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_quant_fp8", "fa_strerror"]
     for n in names:
         assert hasattr(fa_lib, n), n
@@ -303,3 +303,29 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_HERE", str(tmp_path))
     with pytest.raises(RuntimeError, match="not built"):
         fa.load_library()
+
+
+def fpaged(lib, q=P, kc=P, vc=P, bt=P, cl=P, o=FAR[0], lse=FAR[1], S=4, H=8, Hkv=2, Nq=100, D=128,
+           BS=16, NB=64, MB=16, scale=0.088, causal=1, dtype=1):
+    return lib.fa_fwd_paged(q, kc, vc, bt, cl, o, lse, S, H, Hkv, Nq, D, BS, NB, MB, scale, causal,
+                            dtype, None)
+
+
+def test_fwd_paged_validation(fa_lib):
+    assert fpaged(fa_lib, q=0) == INVALID
+    assert fpaged(fa_lib, cl=0) == INVALID
+    assert fpaged(fa_lib, Nq=0) == INVALID
+    assert fpaged(fa_lib, NB=0) == INVALID
+    assert fpaged(fa_lib, Hkv=3) == INVALID             # 8 % 3 != 0
+    assert fpaged(fa_lib, scale=float("nan")) == INVALID
+    assert fpaged(fa_lib, dtype=7) == INVALID
+    assert fpaged(fa_lib, dtype=0) == UNSUPPORTED       # fp32 caches
+    assert fpaged(fa_lib, D=64) == UNSUPPORTED
+    assert fpaged(fa_lib, BS=32) == UNSUPPORTED
+    assert fpaged(fa_lib, NB=1 << 17, Hkv=8) == UNSUPPORTED   # one cache of 4 GiB
+    assert fpaged(fa_lib, MB=1 << 25) == UNSUPPORTED          # 16 * MB past 2^29
+    assert fpaged(fa_lib, q=P + 8) == ALIGN
+    assert fpaged(fa_lib, bt=P + 2) == ALIGN
+    assert fpaged(fa_lib, lse=FAR[1] + 2) == ALIGN
+    assert fpaged(fa_lib, o=P) == INVALID                 # o overlaps q
+    assert fpaged(fa_lib, lse=FAR[0] + 64) == INVALID     # lse overlaps o

@@ -6,7 +6,8 @@ call only enqueues kernels on its stream.  Two checks, on small shapes:
   - each entry point on a second stream (ordered after the inputs' stream)
     returns the same bits as on the current stream;
   - one captured graph of the forward, the backward, the FP8 quantiser and
-    forward, a masked forward with its block map and the paged decode,
+    forward, a masked forward with its block map, the paged decode and the
+    chunked prefill over the paged cache,
     replayed three times with new inputs written eagerly between replays,
     returns on every replay the same bits as the eager calls on those inputs.
 The kernels use no atomics, so equal inputs give equal bits.
@@ -50,6 +51,7 @@ class Case:
         d = inputs.decode_inputs(dc, context_lens=[1, 250, 400])
         self.dec = {n: d[n].to(dev) for n in ("q", "k_cache", "v_cache", "block_tables", "context_lens")}
         self.dec_max = d["max_context_len"]
+        self.pre_q = inputs.normal(seed + 7, (3, 4, 64, D), 1.0, d["q"].dtype).to(dev)
         self.dec_scale = float(np.float32(dc.scale))
         self.scale = float(np.float32(1.0 / np.sqrt(D)))
         f32 = torch.float32
@@ -57,7 +59,7 @@ class Case:
         self.out = dict(o=z(B, H, N, D), lse=z(B, H, N), dq=z(B, H, N, D), dk=z(B, H, N, D),
                         dv=z(B, H, N, D), o8=z(B, H, N, D), lse8=z(B, H, N), ox=z(B, H, N, D),
                         lx=z(B, H, N), mblk=z(self.mwords, dt=torch.int32),
-                        dout_dec=torch.zeros_like(self.dec["q"]))
+                        dout_dec=torch.zeros_like(self.dec["q"]), opre=z(3, 4, 64, D), lpre=z(3, 4, 64))
         self.bws = z(fa.fa_bwd_workspace_size(B, H, N), dt=torch.uint8)
         self.dws = z(fa.fa_paged_decode_workspace_size(3, 4, D, self.dec_max), dt=torch.uint8)
         nb = lambda lay: fa.fa_fp8_codes_bytes(B, H, N, D, lay)
@@ -71,6 +73,8 @@ class Case:
             t.copy_(inputs.normal(seed + i, tuple(t.shape), 1.0, bf).to(self.dev))
         self.dec["q"].copy_(inputs.normal(seed + 9, tuple(self.dec["q"].shape), 1.0,
                                           self.dec["q"].dtype).to(self.dev))
+        self.pre_q.copy_(inputs.normal(seed + 10, tuple(self.pre_q.shape), 1.0,
+                                       self.pre_q.dtype).to(self.dev))
 
     def run(self, stream=None):
         """Enqueue every entry point on stream (None: torch's current stream)."""
@@ -90,6 +94,9 @@ class Case:
         fa.fa_paged_decode(dd["q"], dd["k_cache"], dd["v_cache"], dd["block_tables"], dd["context_lens"],
                            o["dout_dec"], 3, 4, 2, D, 16, dd["block_tables"].shape[1], self.dec_max,
                            self.dec_scale, self.dws, stream=stream)
+        fa.fa_fwd_paged(self.pre_q, dd["k_cache"], dd["v_cache"], dd["block_tables"], dd["context_lens"],
+                        o["opre"], o["lpre"], 3, 4, 2, 64, D, 16, dd["k_cache"].shape[0],
+                        dd["block_tables"].shape[1], self.dec_scale, True, stream=stream)
 
     def snapshot(self):
         return {n: t.clone() for n, t in self.out.items()}
@@ -140,5 +147,6 @@ def test_graph_replay(gpu, fa_lib):
         g.replay()
         torch.cuda.synchronize()
         got = c.snapshot()
-        assert all(torch.isfinite(t.float()).all() for n, t in got.items() if n not in ("lse", "lx", "lse8")), rep
+        assert all(torch.isfinite(t.float()).all() for n, t in got.items()
+                   if n not in ("lse", "lx", "lse8", "lpre")), rep
         assert_same(want, got, "replay %d" % rep)
