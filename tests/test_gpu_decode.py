@@ -59,6 +59,21 @@ def test_edge_context_lengths(gpu, fa_lib, dt, Hkv):
     assert torch.all(out[0] == 0)  # empty context
 
 
+# more than 16 partitions of 256 tokens: the merge combines its chunks of 16
+# partitions online (4097 -> 17 partitions, 8192 -> 32, 8193 -> 33, 65553 -> 257)
+LONG_CTX = [4097, 4352, 8191, 8192, 8193, 20000, 65553]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("Hkv", [4, 2])
+def test_long_contexts_many_partitions(gpu, fa_lib, dt, Hkv):
+    cfg = inputs.DecodeConfig(cid=94, num_seqs=len(LONG_CTX), num_heads=4, num_kv_heads=Hkv,
+                              num_blocks=7600, ctx_lo=1, ctx_hi=max(LONG_CTX),
+                              dtype=torch.float16 if dt == "f16" else torch.bfloat16)
+    d = inputs.decode_inputs(cfg, context_lens=LONG_CTX)
+    check(d, cfg, gpu, "long contexts %s Hkv%d" % (dt, Hkv))
+
+
 @pytest.mark.parametrize("H,Hkv", [(12, 4), (8, 1), (32, 2), (16, 8)],
                          ids=["G3", "MQA-G8", "G16", "G2"])
 def test_grouped_query_heads(gpu, fa_lib, H, Hkv):
