@@ -119,7 +119,7 @@ def main():
                          "(reference kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -147,7 +147,7 @@ def main():
     torch.cuda.set_device(dev)
 
     # ---------------- inputs (host, seeded) -> HBM
-    fcfg = inputs.FWD_CONFIGS[3]
+    fcfg = inputs.FWD_CAUSAL_N8192
     log("generating forward inputs: " + fcfg.name)
     q, k, v = inputs.fwd_inputs(fcfg)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)

@@ -18,7 +18,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-__all__ = ["FwdConfig", "FWD_CONFIGS", "DecodeConfig", "DECODE_CONFIG", "normal",
+__all__ = ["FwdConfig", "FWD_CONFIGS", "FWD_FP32_N256", "FWD_BF16_N2048", "FWD_CAUSAL_N8192",
+           "FWD_CAUSAL_N65536", "DecodeConfig", "DECODE_CONFIG", "normal",
            "fwd_inputs", "bwd_dout", "sample_rows", "decode_inputs", "prefill_queries",
            "PREFILL_CONFIG", "PREFILL_NQ"]
 
@@ -64,7 +65,12 @@ FWD_CONFIGS = {
     4: FwdConfig(4, 1, 8, 65536, 128, torch.bfloat16, True, 2.0,
                  "B1 H8 N65536 d128 bf16 causal, Q,K x2"),
 }
-# grouped-query forward: config 3 with 8 kv heads (4 query heads per kv head)
+# the forward workloads by what they are
+FWD_FP32_N256 = FWD_CONFIGS[1]
+FWD_BF16_N2048 = FWD_CONFIGS[2]
+FWD_CAUSAL_N8192 = FWD_CONFIGS[3]    # the benchmark's forward workload
+FWD_CAUSAL_N65536 = FWD_CONFIGS[4]
+# grouped-query forward: the causal N=8192 workload with 8 kv heads (4 query heads per kv head)
 FWD_GQA_CONFIG = FwdConfig(7, 2, 32, 8192, 128, torch.bfloat16, True, 1.0,
                            "B2 H32 Hkv8 N8192 d128 bf16 causal", Hkv=8)
 

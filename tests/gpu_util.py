@@ -32,7 +32,7 @@ FP8_TOL = dict(rel=2.0 ** -4, abs=2.0 ** -8, lse_max=1e-3)
 
 
 _LOG = os.environ.get("FA_PROGRESS_LOG") or os.path.join(
-    os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out", "gpu_progress.log")
+    os.path.dirname(os.path.dirname(os.path.abspath(__file__))), ".test_progress", "gpu_progress.log")
 
 
 def progress(msg):

@@ -124,7 +124,7 @@ def check_sampled(cfg, dev, heads):
 
 
 def test_headline_sampled(gpu, fa_lib):
-    check_sampled(inputs.FWD_CONFIGS[3], gpu, [(0, 0), (1, 31)])
+    check_sampled(inputs.FWD_CAUSAL_N8192, gpu, [(0, 0), (1, 31)])
 
 
 def test_gqa_headline_sampled(gpu, fa_lib):

@@ -131,14 +131,14 @@ def test_tril_mask_equals_causal(gpu, fa_lib):
 
 
 def test_headline_sliding_window_sampled(gpu, fa_lib):
-    cfg = inputs.FWD_CONFIGS[3]
+    cfg = inputs.FWD_CAUSAL_N8192
     q, k, v = inputs.fwd_inputs(cfg)
     rows = inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5)
     check(q, k, v, True, (1024, -1), None, gpu, "B2 H32 N8192 window 1024", rows=rows)
 
 
 def test_headline_boolean_mask_sampled(gpu, fa_lib):
-    cfg = inputs.FWD_CONFIGS[3]
+    cfg = inputs.FWD_CAUSAL_N8192
     q, k, v = inputs.fwd_inputs(cfg)
     N = cfg.N
     # block-sparse causal pattern: each 64-key block is kept with probability 1/2
@@ -235,7 +235,7 @@ def test_boolean_masks_with_block_map(gpu, fa_lib, dt, prefix, Nq, Nk, causal, w
 
 
 def test_headline_block_sparse_mask_with_map_sampled(gpu, fa_lib):
-    cfg = inputs.FWD_CONFIGS[3]
+    cfg = inputs.FWD_CAUSAL_N8192
     q, k, v = inputs.fwd_inputs(cfg)
     N = cfg.N
     keep = torch.from_numpy(np.random.default_rng(64).random((N // 128, N // 64)) < 0.5)

@@ -102,5 +102,5 @@ def test_fwd_fp8_deterministic(gpu, fa_lib):
 
 
 def test_fwd_fp8_headline_sampled(gpu, fa_lib):
-    cfg = inputs.FWD_CONFIGS[3]
+    cfg = inputs.FWD_CAUSAL_N8192
     run_fp8(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5), label=cfg.name)

@@ -45,12 +45,12 @@ def check_cfg(cfg, dev, rows=None, label=None):
 
 
 def test_config1_fp32(gpu, fa_lib):
-    check_cfg(inputs.FWD_CONFIGS[1], gpu)
+    check_cfg(inputs.FWD_FP32_N256, gpu)
 
 
 @pytest.mark.parametrize("N", [2048, 2000])
 def test_config2_bf16(gpu, fa_lib, N):
-    check_cfg(inputs.FWD_CONFIGS[2].replace(N=N), gpu)
+    check_cfg(inputs.FWD_BF16_N2048.replace(N=N), gpu)
 
 
 @pytest.mark.parametrize("dt,d,H,Hkv,causal", [
@@ -69,12 +69,12 @@ def test_gqa_headline_sampled_rows(gpu, fa_lib):
 
 
 def test_config3_headline_sampled_rows(gpu, fa_lib):
-    cfg = inputs.FWD_CONFIGS[3]
+    cfg = inputs.FWD_CAUSAL_N8192
     check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
 
 
 def test_config4_long_context_sampled_rows(gpu, fa_lib):
-    cfg = inputs.FWD_CONFIGS[4]
+    cfg = inputs.FWD_CAUSAL_N65536
     check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
 
 
