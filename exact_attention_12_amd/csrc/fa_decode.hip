@@ -362,22 +362,29 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
             const int tb = b * kDecBS + 8 * (lane % 2);
             const int nvalid = ntok - tb;
             // tokens >= ntok are outside the context (their cache slots may
-            // hold anything): their values are replaced by 0, and p_t = 0
-            float vf[4][8];
+            // hold anything): their value halves are cleared, and p_t = 0
+            u32x4 vv[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < 4; ++c) vv[c] = vr[i][c];
+            if (nvalid < 8) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vf[c][e] = (e < nvalid) ? vec_elem<T>(vr[i][c], e) : 0.f;
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        vv[c][e] &= (2 * e < nvalid ? 0xffffu : 0u) | (2 * e + 1 < nvalid ? 0xffff0000u : 0u);
+            }
 #pragma unroll
             for (int g = 0; g < GM; ++g) {
                 if (g < ng) {
+                    // p rounded to the cache type, as the PagedAttention kernel
+                    // does before its value dot ("LV"), then two tokens per
+                    // dot instruction with fp32 accumulation
                     const f32x4 pa = *(const f32x4 *)(&logits[g][tb]);
                     const f32x4 pb = *(const f32x4 *)(&logits[g][tb + 4]);
-                    const float pw[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+                    const u32x4 pp = {Mma<T>::pack2(pa[0], pa[1]), Mma<T>::pack2(pa[2], pa[3]),
+                                      Mma<T>::pack2(pb[0], pb[1]), Mma<T>::pack2(pb[2], pb[3])};
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[g][c] = __builtin_fmaf(pw[e], vf[c][e], acc[g][c]);
+                    for (int c = 0; c < 4; ++c) acc[g][c] = dot8<T>(pp, vv[c], acc[g][c]);
                 }
             }
         }
