@@ -103,6 +103,32 @@ def test_paged_prefill_equals_contiguous_ext(gpu, fa_lib):
     assert (o1 - o2).abs().max().item() <= 1e-5 and (l1 - l2).abs().max().item() <= 1e-5
 
 
+def test_full_prefill_equals_square_causal_forward(gpu, fa_lib):
+    """Nq = context length: the whole context is new, the mask is fa_fwd's square causal one."""
+    n = 1000
+    cfg = inputs.DecodeConfig(cid=93, num_seqs=2, num_heads=8, num_kv_heads=8, num_blocks=200,
+                              ctx_lo=1, ctx_hi=n, dtype=torch.bfloat16)
+    o1, l1 = run_case(gpu, cfg, [n, n], n, True, "full prefill")
+    d = inputs.decode_inputs(cfg, context_lens=[n, n])
+    q = inputs.prefill_queries(cfg, n)
+    nb = (n + 15) // 16
+    Ks, Vs = [], []
+    for s in range(2):
+        bt = d["block_tables"][s, :nb].long()
+        Ks.append(d["k_cache"][bt].permute(1, 0, 3, 2, 4).reshape(8, nb * 16, 128)[:, :n])
+        Vs.append(d["v_cache"][bt].permute(1, 0, 3, 2).reshape(8, nb * 16, 128)[:, :n])
+    o2, l2 = fa.forward(q.to(gpu), torch.stack(Ks).contiguous().to(gpu), torch.stack(Vs).contiguous().to(gpu),
+                        causal=True)
+    torch.cuda.synchronize()
+    assert (o1 - o2).abs().max().item() <= 1e-5 and (l1 - l2).abs().max().item() <= 1e-5
+
+
+def test_multi_query_prefill(gpu, fa_lib):
+    cfg = inputs.DecodeConfig(cid=95, num_seqs=3, num_heads=32, num_kv_heads=1, num_blocks=300,
+                              ctx_lo=1, ctx_hi=1500, dtype=torch.float16)
+    run_case(gpu, cfg, [129, 700, 1500], 129, True, "multi-query 32/1")
+
+
 def test_headline_paged_prefill_sampled(gpu, fa_lib):
     cfg = inputs.PREFILL_CONFIG
     rng = np.random.default_rng(1000 * cfg.cid + 3)
