@@ -245,13 +245,22 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
         const int k0 = j * BC;
         char *kd = smem + buf * STAGEB;
         char *vd = kd + KTILEB;
+        if (k0 + BC <= N) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int I = wave * 2 + i;
-            // keys past the end re-read key N-1 (finite; masked below)
-            const int over = k0 + k_row[i] - (N - 1);
-            buffer_load_lds16(krs, kd + I * 1024, over > 0 ? k_off[i] - over * KROWB : k_off[i], k0 * KROWB);
-            buffer_load_lds16(vrs, vd + I * 1024, v_off[i], j * VTILEB);
+            for (int i = 0; i < 2; ++i) {
+                const int I = wave * 2 + i;
+                buffer_load_lds16(krs, kd + I * 1024, k_off[i], k0 * KROWB);
+                buffer_load_lds16(vrs, vd + I * 1024, v_off[i], j * VTILEB);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int I = wave * 2 + i;
+                // keys past the end re-read key N-1 (finite; masked below)
+                const int over = k0 + k_row[i] - (N - 1);
+                buffer_load_lds16(krs, kd + I * 1024, over > 0 ? k_off[i] - over * KROWB : k_off[i], k0 * KROWB);
+                buffer_load_lds16(vrs, vd + I * 1024, v_off[i], j * VTILEB);
+            }
         }
     };
     // per-lane LDS read offsets: K row fragment (row col of block kb, bytes
@@ -297,6 +306,10 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
         float l_run = 0.f;       // sum of the unrounded P~ (unshifted)
 
         load_tile(0, 0);
+        // block scale exponents of the tile being processed; those of the
+        // next tile are read one tile ahead so that the scalar load latency
+        // hides behind the tile's work
+        int ke_next = KEh[0], ve_next = VEh[0];
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
@@ -306,8 +319,8 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
             const int k0 = j * BC;
             const char *Ks = smem + STAGE * STAGEB;
             const char *Vs = Ks + KTILEB;
-            const float c = ldexpf(cq, KEh[k0 / QBLK]);
-            const int vsh = VEh[k0 / QBLK] - evmax;  // <= 0: V block scale relative to the largest
+            const float c = ldexpf(cq, ke_next);
+            const int vsh = ve_next - evmax;  // <= 0: V block scale relative to the largest
 
             // S^T = K Q^T: lane (col = query, h), register r of block kb holds
             // tile key 32h + 16kb + r
@@ -326,6 +339,11 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
                 }
             }
             __builtin_amdgcn_s_setprio(0);
+            {
+                const int nb = min((k0 + BC) / QBLK, nblk - 1);
+                ke_next = KEh[nb];
+                ve_next = VEh[nb];
+            }
 
             // masks: key k0 + 32h + 16kb + r is visible iff 16kb + r <= lim
             const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > wq_lo);
@@ -378,12 +396,16 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
             l_run += ldexpf(rs, -vsh);
 
             // P' as E4M3: byte 16kb + r of the lane's 32 is register r of block kb
+            // (the first conversion of a word writes its low half and the
+            // second its high half, so the word's prior contents never show)
             i32x8 pb;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][4 * w], p[kb][4 * w + 1], 0, false);
+                    int undef_word;
+                    asm volatile("" : "=v"(undef_word));
+                    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][4 * w], p[kb][4 * w + 1], undef_word, false);
                     pb[4 * kb + w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][4 * w + 2], p[kb][4 * w + 3], lo, true);
                 }
             // O^T += V^T P'^T: lane (col = d row of the block, h) reads bytes
