@@ -135,13 +135,50 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // resident on one XCD (sharing its L2) work on the same head.
     int wid = blockIdx.x;
     const int G = gridDim.x;
-    if (G % 8 == 0) wid = (wid % 8) * (G / 8) + wid / 8;
     // Causal: workgroup p of a head takes the query tiles nqt-1-p (heavy)
     // and p (light) one after the other, so that every workgroup has about
     // the same work and the grid drains evenly.
     const int wg_per_head = CAUSAL ? (num_qtiles + 1) / 2 : num_qtiles;
-    const int bh = wid / wg_per_head;
-    const int pi = wid % wg_per_head;
+    int bh, pi;
+    if constexpr (EXT == 4) {
+        // Sequences differ in length, so a contiguous share of the grid per
+        // XCD would leave the XCDs unevenly loaded.  Instead the units
+        // (sequence, kv head) are dealt round-robin over the XCDs: with 8 | S*Hkv
+        // XCD x takes units x, x+8, ..., each unit's group * nqt workgroups in
+        // a row (they read the same K/V through that XCD's L2).  Sequences go
+        // longest first (ranked from the context lengths, up to 64
+        // sequences), so that the short ones fill the grid's tail.
+        const int W = group * wg_per_head;
+        const int units = G / W;
+        const int hkv = H / group;
+        int u = wid, r = 0;
+        if (units % 8 == 0) {
+            const int t = wid / 8;
+            u = (t / W) * 8 + wid % 8;
+            r = t % W;
+        } else {
+            u = wid / W;
+            r = wid % W;
+        }
+        int seq = u / hkv;
+        const int S = units / hkv;
+        if (S <= kWave) {
+            const int mine = lane < S ? ext.ctx_lens[lane] : INT_MIN;
+            int rank = 0;
+            for (int j = 0; j < S; ++j) {
+                const int cj = __builtin_amdgcn_readlane(mine, j);
+                rank += (cj > mine || (cj == mine && j < lane)) ? 1 : 0;
+            }
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < S && rank == seq);
+            seq = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+        }
+        bh = seq * H + (u % hkv) * group + r / wg_per_head;
+        pi = r % wg_per_head;
+    } else {
+        if (G % 8 == 0) wid = (wid % 8) * (G / 8) + wid / 8;
+        bh = wid / wg_per_head;
+        pi = wid % wg_per_head;
+    }
 
     // keys of this head and the diagonal's offset (paged: per sequence)
     int NK = EXT ? ext.Nk : N;

@@ -134,3 +134,21 @@ def test_headline_paged_prefill_sampled(gpu, fa_lib):
     rng = np.random.default_rng(1000 * cfg.cid + 3)
     ctx = rng.integers(cfg.ctx_lo, cfg.ctx_hi + 1, size=cfg.num_seqs)
     run_case(gpu, cfg, ctx, inputs.PREFILL_NQ, True, "16 seqs x 512 new tokens", seqs=[0, 7, 15])
+
+
+def test_prefill_equal_context_lengths(gpu, fa_lib):
+    # workgroups go longest sequence first; equal lengths must still give every
+    # (sequence, head, query tile) exactly one workgroup
+    cfg = inputs.DecodeConfig(cid=96, num_seqs=8, num_heads=4, num_kv_heads=2, num_blocks=300,
+                              ctx_lo=1, ctx_hi=1000, dtype=torch.bfloat16)
+    run_case(gpu, cfg, [300, 300, 17, 300, 17, 1000, 1000, 20], 20, True, "equal lengths")
+
+
+@pytest.mark.parametrize("S,Hkv", [(72, 1), (70, 2)])
+def test_prefill_many_sequences(gpu, fa_lib, S, Hkv):
+    # more sequences than one wave ranks (kept in order), with and without
+    # 8 | S * Hkv
+    cfg = inputs.DecodeConfig(cid=97, num_seqs=S, num_heads=2, num_kv_heads=Hkv, num_blocks=1200,
+                              ctx_lo=1, ctx_hi=200, dtype=torch.float16)
+    ctx = np.random.default_rng(97 + S).integers(1, 201, size=S)
+    run_case(gpu, cfg, ctx, 5, True, "S=%d Hkv=%d" % (S, Hkv))
