@@ -144,10 +144,10 @@ def test_prefill_equal_context_lengths(gpu, fa_lib):
     run_case(gpu, cfg, [300, 300, 17, 300, 17, 1000, 1000, 20], 20, True, "equal lengths")
 
 
-@pytest.mark.parametrize("S,Hkv", [(72, 1), (70, 2)])
+@pytest.mark.parametrize("S,Hkv", [(64, 1), (72, 1), (70, 2)])
 def test_prefill_many_sequences(gpu, fa_lib, S, Hkv):
-    # more sequences than one wave ranks (kept in order), with and without
-    # 8 | S * Hkv
+    # as many sequences as one wave ranks (64), and more (kept in order), with
+    # and without 8 | S * Hkv
     cfg = inputs.DecodeConfig(cid=97, num_seqs=S, num_heads=2, num_kv_heads=Hkv, num_blocks=1200,
                               ctx_lo=1, ctx_hi=200, dtype=torch.float16)
     ctx = np.random.default_rng(97 + S).integers(1, 201, size=S)
