@@ -365,7 +365,7 @@ def main():
 
     fwd_hash = source_hash("fa_fwd.hip", "fa_device.h", "fa_tile.h")
     bwd_hash = source_hash("fa_bwd.hip", "fa_device.h", "fa_tile.h")
-    dec_hash = source_hash("fa_decode.hip", "fa_device.h")
+    dec_hash = source_hash("fa_decode.hip", "fa_device.h", "fa_tile.h")
     fwd_traffic = measured_traffic("fa_fwd_kernel", fwd_hash)
     dec_traffic = measured_traffic("fa_decode_partition_kernel", dec_hash)
     bwd_traffic = measured_traffic("fa_bwd", bwd_hash)
