@@ -58,18 +58,14 @@ class FwdConfig:
         return FwdConfig(**args)
 
 
-FWD_CONFIGS = {
-    1: FwdConfig(1, 1, 1, 256, 64, torch.float32, False, 1.0, "B1 H1 N256 d64 fp32"),
-    2: FwdConfig(2, 4, 16, 2048, 64, torch.bfloat16, False, 1.0, "B4 H16 N2048 d64 bf16"),
-    3: FwdConfig(3, 2, 32, 8192, 128, torch.bfloat16, True, 1.0, "B2 H32 N8192 d128 bf16 causal"),
-    4: FwdConfig(4, 1, 8, 65536, 128, torch.bfloat16, True, 2.0,
-                 "B1 H8 N65536 d128 bf16 causal, Q,K x2"),
-}
-# the forward workloads by what they are
-FWD_FP32_N256 = FWD_CONFIGS[1]
-FWD_BF16_N2048 = FWD_CONFIGS[2]
-FWD_CAUSAL_N8192 = FWD_CONFIGS[3]    # the benchmark's forward workload
-FWD_CAUSAL_N65536 = FWD_CONFIGS[4]
+# the forward workloads, named by what they are (the first field seeds the inputs)
+FWD_FP32_N256 = FwdConfig(1, 1, 1, 256, 64, torch.float32, False, 1.0, "B1 H1 N256 d64 fp32")
+FWD_BF16_N2048 = FwdConfig(2, 4, 16, 2048, 64, torch.bfloat16, False, 1.0, "B4 H16 N2048 d64 bf16")
+FWD_CAUSAL_N8192 = FwdConfig(3, 2, 32, 8192, 128, torch.bfloat16, True, 1.0,
+                             "B2 H32 N8192 d128 bf16 causal")  # the benchmark's forward workload
+FWD_CAUSAL_N65536 = FwdConfig(4, 1, 8, 65536, 128, torch.bfloat16, True, 2.0,
+                              "B1 H8 N65536 d128 bf16 causal, Q,K x2")
+FWD_CONFIGS = {c.cid: c for c in (FWD_FP32_N256, FWD_BF16_N2048, FWD_CAUSAL_N8192, FWD_CAUSAL_N65536)}
 # grouped-query forward: the causal N=8192 workload with 8 kv heads (4 query heads per kv head)
 FWD_GQA_CONFIG = FwdConfig(7, 2, 32, 8192, 128, torch.bfloat16, True, 1.0,
                            "B2 H32 Hkv8 N8192 d128 bf16 causal", Hkv=8)
