@@ -40,9 +40,9 @@ def check(d, cfg, dev, label):
     return out
 
 
-def test_config5_full(gpu, fa_lib):
+def test_decode_64x32_full(gpu, fa_lib):
     cfg = inputs.DECODE_CONFIG
-    check(inputs.decode_inputs(cfg), cfg, gpu, "config5")
+    check(inputs.decode_inputs(cfg), cfg, gpu, "64 seqs x 32 heads")
 
 
 EDGE_CTX = [0, 1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000, 2049, 4096]

@@ -44,12 +44,12 @@ def check_cfg(cfg, dev, rows=None, label=None):
     return assert_fwd_close(o, lse, o_ref, l_ref, cfg.dtype, label)
 
 
-def test_config1_fp32(gpu, fa_lib):
+def test_fp32_N256(gpu, fa_lib):
     check_cfg(inputs.FWD_FP32_N256, gpu)
 
 
 @pytest.mark.parametrize("N", [2048, 2000])
-def test_config2_bf16(gpu, fa_lib, N):
+def test_bf16_N2048(gpu, fa_lib, N):
     check_cfg(inputs.FWD_BF16_N2048.replace(N=N), gpu)
 
 
@@ -68,12 +68,12 @@ def test_gqa_headline_sampled_rows(gpu, fa_lib):
     check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
 
 
-def test_config3_headline_sampled_rows(gpu, fa_lib):
+def test_causal_N8192_sampled_rows(gpu, fa_lib):
     cfg = inputs.FWD_CAUSAL_N8192
     check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
 
 
-def test_config4_long_context_sampled_rows(gpu, fa_lib):
+def test_causal_N65536_sampled_rows(gpu, fa_lib):
     cfg = inputs.FWD_CAUSAL_N65536
     check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
 
