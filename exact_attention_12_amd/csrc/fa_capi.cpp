@@ -360,12 +360,14 @@ extern "C" size_t fa_paged_decode_workspace_size(int num_seqs, int num_heads, in
     return fa::decode_workspace_bytes(num_seqs, num_heads, max_context_len);
 }
 
-extern "C" int fa_paged_decode(const void *q, const void *k_cache, const void *v_cache,
-                               const int32_t *block_tables, const int32_t *context_lens,
-                               void *out, int num_seqs, int num_heads, int num_kv_heads,
-                               int head_size, int block_size, int max_blocks_per_seq,
-                               int max_context_len, float scale, int dtype, void *workspace,
-                               size_t workspace_bytes, void *stream)
+namespace {
+
+// Validation of fa_paged_decode's arguments other than the workspace; on
+// success *need is the workspace the sizes call for.
+int decode_args(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *block_tables, const int32_t *context_lens, const void *out,
+                int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+                int max_blocks_per_seq, int max_context_len, float scale, int dtype, size_t *need)
 {
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
         return FA_ERR_INVALID_ARG;
@@ -375,7 +377,8 @@ extern "C" int fa_paged_decode(const void *q, const void *k_cache, const void *v
     if (num_heads % num_kv_heads != 0) return FA_ERR_INVALID_ARG;
     if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return FA_ERR_INVALID_ARG;
     if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
-    if (elem_bytes(dtype) == 0) return FA_ERR_INVALID_ARG;
+    const int es = elem_bytes(dtype);
+    if (es == 0) return FA_ERR_INVALID_ARG;
     if (dtype == FA_F32 || head_size != 128 || block_size != 16) return FA_ERR_UNSUPPORTED;
     const int64_t nparts =
         ((int64_t)max_context_len + FA_DECODE_PARTITION_TOKENS - 1) / FA_DECODE_PARTITION_TOKENS;
@@ -383,9 +386,41 @@ extern "C" int fa_paged_decode(const void *q, const void *k_cache, const void *v
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return FA_ERR_ALIGNMENT;
-    const size_t need = fa::decode_workspace_bytes(num_seqs, num_heads, max_context_len);
+    // out must not overlap what the call reads (the caches' extent is not
+    // passed, so they cannot be checked here)
+    const uint64_t qo_bytes = (uint64_t)num_seqs * num_heads * head_size * es;
+    const uint64_t bt_bytes = (uint64_t)num_seqs * max_blocks_per_seq * 4;
+    const uint64_t cl_bytes = (uint64_t)num_seqs * 4;
+    if (overlap(out, qo_bytes, q, qo_bytes) || overlap(out, qo_bytes, block_tables, bt_bytes) ||
+        overlap(out, qo_bytes, context_lens, cl_bytes))
+        return FA_ERR_INVALID_ARG;
+    *need = fa::decode_workspace_bytes(num_seqs, num_heads, max_context_len);
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_paged_decode(const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               void *out, int num_seqs, int num_heads, int num_kv_heads,
+                               int head_size, int block_size, int max_blocks_per_seq,
+                               int max_context_len, float scale, int dtype, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    size_t need = 0;
+    const int st = decode_args(q, k_cache, v_cache, block_tables, context_lens, out, num_seqs,
+                               num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                               max_context_len, scale, dtype, &need);
+    if (st != FA_OK) return st;
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return FA_ERR_ALIGNMENT;
+    // the workspace is written: it must not overlap q, the tables, the
+    // context lengths or out
+    const uint64_t qo_bytes = (uint64_t)num_seqs * num_heads * head_size * elem_bytes(dtype);
+    if (overlap(workspace, need, q, qo_bytes) || overlap(workspace, need, out, qo_bytes) ||
+        overlap(workspace, need, block_tables, (uint64_t)num_seqs * max_blocks_per_seq * 4) ||
+        overlap(workspace, need, context_lens, (uint64_t)num_seqs * 4))
+        return FA_ERR_INVALID_ARG;
     const hipError_t e = fa::decode_dispatch(q, k_cache, v_cache, block_tables, context_lens, out,
                                              num_seqs, num_heads, num_kv_heads, max_blocks_per_seq,
                                              max_context_len, scale, dtype, workspace,

@@ -353,7 +353,10 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int num_heads, int head_size
  *                  sequence s lives in physical block block_tables[s][t /
  *                  block_size], slot t % block_size.
  *   context_lens : [num_seqs] int32, each in [0, max_context_len].  Not
- *                  checked on the device: larger values read out of range.
+ *                  checked on the device: the grid covers
+ *                  ceil(max_context_len / FA_DECODE_PARTITION_TOKENS)
+ *                  partitions, so tokens of a larger value past that range
+ *                  are left out of its softmax.
  *   out          : [num_seqs, num_heads, head_size], element type `dtype`.
  *                  out[s,h,:] = sum_t p_t V_t with p = softmax_t(scale * q[s,h]
  *                  . K_t) over t < context_lens[s], rounded to nearest even.
@@ -369,6 +372,9 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int num_heads, int head_size
  *                  is written.  Concurrent calls need separate workspaces.
  * The first ceil(context_lens[s] / block_size) entries of each table row must
  * be valid block ids; they are not checked on the device.
+ * out and workspace must not overlap q, block_tables, context_lens or each
+ * other (FA_ERR_INVALID_ARG); the caches' extent is not passed, so overlap
+ * with them is the caller's to avoid.
  */
 int fa_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, const int32_t *context_lens, void *out,

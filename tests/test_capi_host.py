@@ -253,8 +253,8 @@ def test_fwd_fp8_validation(fa_lib):
     assert fwd8(fa_lib, B=1 << 16, H=1 << 16, Hkv=1, N=1 << 10) == UNSUPPORTED
 
 
-def dec(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=P, S=4, H=8, Hkv=8, D=128, BS=16, MB=4,
-        maxctx=64, scale=0.088, dtype=2, ws=P, wsb=1 << 20):
+def dec(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=FAR[0], S=4, H=8, Hkv=8, D=128, BS=16, MB=4,
+        maxctx=64, scale=0.088, dtype=2, ws=FAR[1], wsb=1 << 20):
     return lib.fa_paged_decode(q, kc, vc, bt, cl, out, S, H, Hkv, D, BS, MB, maxctx, scale,
                                dtype, ws, wsb, None)
 
@@ -276,7 +276,15 @@ def test_decode_validation(fa_lib):
     assert dec(fa_lib, cl=P + 2) == ALIGN
     assert dec(fa_lib, ws=0) == WORKSPACE
     assert dec(fa_lib, wsb=16) == WORKSPACE
-    assert dec(fa_lib, ws=P + 16) == ALIGN
+    assert dec(fa_lib, ws=FAR[1] + 16) == ALIGN
+    # out and the workspace are written: neither may overlap what is read, nor each other
+    assert dec(fa_lib, out=P) == INVALID                  # out overlaps q (and the tables)
+    assert dec(fa_lib, out=FAR[2], bt=FAR[2] + 256) == INVALID    # out overlaps block_tables
+    assert dec(fa_lib, out=FAR[2], cl=FAR[2] + 1024) == INVALID   # out overlaps context_lens
+    assert dec(fa_lib, ws=P) == INVALID                   # workspace overlaps q
+    assert dec(fa_lib, ws=FAR[0]) == INVALID              # workspace overlaps out
+    assert dec(fa_lib, ws=FAR[2], bt=FAR[2] + 512) == INVALID     # workspace overlaps the tables
+    assert dec(fa_lib, ws=FAR[2], cl=FAR[2] + 4096) == INVALID    # workspace overlaps context_lens
 
 
 def test_workspace_size(fa_lib):
