@@ -20,7 +20,8 @@ import torch
 
 __all__ = ["FwdConfig", "FWD_CONFIGS", "FWD_FP32_N256", "FWD_BF16_N2048", "FWD_CAUSAL_N8192",
            "FWD_CAUSAL_N65536", "DecodeConfig", "DECODE_CONFIG", "normal",
-           "fwd_inputs", "bwd_dout", "sample_rows", "decode_inputs", "prefill_queries",
+           "fwd_inputs", "bwd_dout", "sample_rows", "sample_rows_per_head", "decode_inputs",
+           "prefill_queries",
            "PREFILL_CONFIG", "PREFILL_NQ"]
 
 
@@ -103,6 +104,42 @@ def sample_rows(N: int, count: int = 256, seed: int = 5) -> np.ndarray:
     rest = np.setdiff1d(np.arange(N, dtype=np.int64), np.array(fixed, dtype=np.int64))
     extra = np.random.default_rng(seed).choice(rest, size=count - len(fixed), replace=False)
     return np.sort(np.concatenate([np.array(fixed, dtype=np.int64), extra]))
+
+
+def sample_rows_per_head(N: int, heads: int, count: int, seed: int, tile: int = 128) -> np.ndarray:
+    """Sorted query rows drawn independently for each of `heads` heads: [heads, count].
+
+    Every head gets {0, 1, 127, 128, N-1} (where < N) and the rest stratified
+    over the `tile`-row query tiles: each tile contributes the same number of
+    distinct rows (tiles drawn at random for the remainder), so with count >=
+    ceil(N / tile) every tile of every head is checked.  Head x draws from
+    PCG64([seed, x]).
+    """
+    if count >= N:
+        return np.tile(np.arange(N, dtype=np.int64), (heads, 1))
+    fixed = sorted({r for r in (0, 1, 127, 128, N - 1) if 0 <= r < N})
+    ntiles = (N + tile - 1) // tile
+    out = np.empty((heads, count), dtype=np.int64)
+    for x in range(heads):
+        rng = np.random.default_rng([seed, x])
+        chosen = set(fixed)
+        need = count - len(chosen)
+        per, extra = divmod(need, ntiles)
+        bonus = set(rng.choice(ntiles, size=extra, replace=False).tolist()) if extra else set()
+        short = 0
+        for t in range(ntiles):
+            lo, hi = t * tile, min(N, (t + 1) * tile)
+            free = np.setdiff1d(np.arange(lo, hi, dtype=np.int64), np.array(sorted(chosen), dtype=np.int64))
+            want = per + (1 if t in bonus else 0)
+            take = min(want, len(free))
+            short += want - take
+            if take:
+                chosen.update(rng.choice(free, size=take, replace=False).tolist())
+        if short:  # a tile had fewer free rows than its share: fill from the rest
+            free = np.setdiff1d(np.arange(N, dtype=np.int64), np.array(sorted(chosen), dtype=np.int64))
+            chosen.update(rng.choice(free, size=short, replace=False).tolist())
+        out[x] = np.sort(np.fromiter(chosen, dtype=np.int64))
+    return out
 
 
 @dataclass(frozen=True)

@@ -85,3 +85,32 @@ def assert_bwd_close(dq, dk, dv, ref, dtype, label=""):
         assert emax <= BWD_TOL["max_rel"] * rmax + BWD_TOL["floor"], (label, name, emax, rmax)
         assert emean <= BWD_TOL["mean_rel"] * rmean + BWD_TOL["floor"], (label, name, emean, rmean)
     return out
+
+
+def oracle_per_head(fn, q, k, v, rows, *args, **kw):
+    """Run an oracle routine head by head, each (b, h) on its own query rows.
+
+    fn(q, k, v, *args, rows=..., **kw) -> (o, lse) is oracle.attention or
+    oracle.attention_ext; q [B, H, N, d], k and v [B, Hkv, Nk, d]; rows
+    [B * H, R] (inputs.sample_rows_per_head).  Query head h reads kv head
+    h // (H // Hkv).  Returns (o [B, H, R, d], lse [B, H, R]) in fp64.
+    """
+    B, H = q.shape[0], q.shape[1]
+    g = H // k.shape[1]
+    R = rows.shape[1]
+    o = np.empty((B, H, R, q.shape[3]), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kvh = h // g
+            o1, l1 = fn(q[b:b + 1, h:h + 1], k[b:b + 1, kvh:kvh + 1], v[b:b + 1, kvh:kvh + 1], *args,
+                        rows=rows[b * H + h], **kw)
+            o[b, h], lse[b, h] = o1[0, 0], l1[0, 0]
+    return o, lse
+
+
+def gather_rows(x, rows):
+    """x [B, H, N, ...] (numpy) at each head's own rows [B * H, R] -> [B, H, R, ...]."""
+    B, H = x.shape[0], x.shape[1]
+    idx = rows.reshape(B, H, -1)
+    return np.take_along_axis(x, idx.reshape(idx.shape + (1,) * (x.ndim - 3)), axis=2)

@@ -1,8 +1,10 @@
 """GPU parity of fa_fwd against the fp64 oracle, through the C ABI.
 
 Full oracle at the small configurations and on a grid of ragged shapes
-(several tiles plus a tail); at the full headline sizes, in the launch
-configuration the benchmark times, 256 sampled query rows per head.
+(several tiles plus a tail); at the full sizes, in the launch configuration
+the benchmark times, sampled query rows drawn independently for every head
+and stratified over its 128-row query tiles: 1,024 rows per head at B=2 H=32
+N=8192 (16 in each query tile) and at B=1 H=8 N=65536 (2 in each query tile).
 """
 import math
 
@@ -13,7 +15,7 @@ import torch
 import exact_attention_12_amd as fa
 import oracle
 from exact_attention_12_amd import inputs
-from gpu_util import TOL, assert_fwd_close, progress
+from gpu_util import TOL, assert_fwd_close, gather_rows, oracle_per_head, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -32,16 +34,23 @@ def run_fwd(q, k, v, scale, causal, dev):
 
 
 def check_cfg(cfg, dev, rows=None, label=None):
+    """rows: None (every row), or [B * H, R] rows of each head (sample_rows_per_head)."""
     label = label or cfg.name
     progress("fa_fwd %s N=%d causal=%d rows=%s" % (label, cfg.N, cfg.causal,
-                                                  "all" if rows is None else len(rows)))
+                                                  "all" if rows is None else "%d per head" % rows.shape[1]))
     q, k, v = inputs.fwd_inputs(cfg)
     scale = float(np.float32(cfg.scale))
     o, lse = run_fwd(q, k, v, scale, cfg.causal, dev)
-    o_ref, l_ref = oracle.attention(q, k, v, scale, cfg.causal, rows=rows)
-    if rows is not None:
-        o, lse = o[:, :, rows], lse[:, :, rows]
+    if rows is None:
+        o_ref, l_ref = oracle.attention(q, k, v, scale, cfg.causal)
+    else:
+        o_ref, l_ref = oracle_per_head(oracle.attention, q, k, v, rows, scale, cfg.causal)
+        o, lse = gather_rows(o, rows), gather_rows(lse, rows)
     return assert_fwd_close(o, lse, o_ref, l_ref, cfg.dtype, label)
+
+
+def head_rows(cfg, count):
+    return inputs.sample_rows_per_head(cfg.N, cfg.B * cfg.H, count, seed=1000 * cfg.cid + 5)
 
 
 def test_fp32_N256(gpu, fa_lib):
@@ -65,17 +74,17 @@ def test_grouped_kv_heads(gpu, fa_lib, dt, d, H, Hkv, causal):
 
 def test_gqa_headline_sampled_rows(gpu, fa_lib):
     cfg = inputs.FWD_GQA_CONFIG
-    check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
+    check_cfg(cfg, gpu, rows=head_rows(cfg, 256))
 
 
 def test_causal_N8192_sampled_rows(gpu, fa_lib):
     cfg = inputs.FWD_CAUSAL_N8192
-    check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
+    check_cfg(cfg, gpu, rows=head_rows(cfg, 1024))
 
 
 def test_causal_N65536_sampled_rows(gpu, fa_lib):
     cfg = inputs.FWD_CAUSAL_N65536
-    check_cfg(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5))
+    check_cfg(cfg, gpu, rows=head_rows(cfg, 1024))
 
 
 DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -159,6 +168,49 @@ def test_P7_P12_first_row_and_single_token(gpu, fa_lib):
     o1, l1 = run_fwd(q[:, :, :1].contiguous(), k[:, :, :1].contiguous(),
                      v[:, :, :1].contiguous(), scale, False, gpu)
     assert np.abs(o1[:, :, 0] - v[:, :, 0].double().numpy()).max() <= 1e-6
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_P3_one_hot_values_expose_P(gpu, fa_lib, dt, causal):
+    # V[j, c] = [j == c0 + c] makes O[i, c] = P[i, c0 + c]; three windows of
+    # d = 128 keys expose every column of P for N = 300 (five 64-key tiles
+    # and a ragged tail), compared with the oracle's P element by element
+    cfg = _cfg(N=300, d=128, causal=causal, dt=DT[dt], cid=83)
+    q, k, _ = inputs.fwd_inputs(cfg)
+    scale = float(np.float32(cfg.scale))
+    P = oracle.probs(q, k, scale, causal)
+    tol = TOL[cfg.dtype]
+    for c0 in range(0, cfg.N, cfg.d):
+        v = torch.zeros(cfg.B, cfg.H, cfg.N, cfg.d)
+        n = min(cfg.d, cfg.N - c0)
+        v[:, :, c0 + torch.arange(n), torch.arange(n)] = 1.0
+        o, _ = run_fwd(q, k, v.to(cfg.dtype), scale, causal, gpu)
+        got, ref = o[..., :n], P[..., c0:c0 + n]
+        err = np.abs(got - ref)
+        progress("P3 %s causal%d keys %d..%d max|dP|=%.3g mean|dP|=%.3g" % (
+            dt, causal, c0, c0 + n - 1, err.max(), err.mean()))
+        assert err.max() <= tol["o_max"] and err.mean() <= tol["o_mean"], (c0, err.max(), err.mean())
+        assert np.all(o[..., n:] == 0), "columns past the one-hot block must be exactly 0"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_P13_convexity(gpu, fa_lib, dt, causal):
+    # each O[i, c] is a convex combination of the values its row sees:
+    # min_j V[j, c] <= O[i, c] <= max_j V[j, c] over the visible keys j
+    cfg = inputs.FwdConfig(cid=84, B=2, H=2, N=333, d=64, dtype=DT[dt], causal=causal, qk_factor=2.0)
+    q, k, v = inputs.fwd_inputs(cfg)
+    o, _ = run_fwd(q, k, v, float(np.float32(cfg.scale)), causal, gpu)
+    vd = v.double().numpy()
+    if causal:
+        lo, hi = np.minimum.accumulate(vd, axis=2), np.maximum.accumulate(vd, axis=2)
+    else:
+        lo, hi = vd.min(2, keepdims=True), vd.max(2, keepdims=True)
+    slack = 1e-5  # the fp32 accumulation and the final division
+    below, above = (lo - slack - o).max(), (o - hi - slack).max()
+    progress("P13 %s causal%d worst excursion below %.3g above %.3g" % (dt, causal, below, above))
+    assert below <= 0 and above <= 0
 
 
 def test_P9_key_permutation_noncausal(gpu, fa_lib):
