@@ -24,13 +24,15 @@ __all__ = [
     "fa_fwd_fp8", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_strerror", "forward",
     "backward", "quant_fp8", "forward_fp8", "paged_decode", "lib_path", "load_library",
     "FA_FP8_BLOCK_ROWS", "FA_MASK_BLOCK_ROWS", "FA_MASK_BLOCK_COLS", "fa_mask_blocks_words",
-    "fa_mask_blocks", "mask_block_map", "fa_fwd_paged", "forward_paged",
+    "fa_mask_blocks", "mask_block_map", "fa_fwd_paged", "forward_paged", "fa_paged_decode_noalloc",
+    "FA_DECODE_NOALLOC_SCRATCH_BYTES",
 ]
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_DECODE_PARTITION_TOKENS = 256  # must match include/fa.h
 FA_MASK_BLOCK_ROWS, FA_MASK_BLOCK_COLS = 128, 64  # must match include/fa.h
 FA_FP8_BLOCK_ROWS = 128           # must match include/fa.h
+FA_DECODE_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # must match include/fa.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -90,6 +92,8 @@ def load_library():
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_paged_decode.restype = i
+    lib.fa_paged_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_paged_decode_noalloc.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -273,6 +277,21 @@ def fa_paged_decode(q, k_cache, v_cache, block_tables, context_lens, out, num_se
         _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise FAError(st, "fa_paged_decode")
+
+
+def fa_paged_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, out, num_seqs,
+                            num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                            max_context_len, scale, dtype=None, stream=None):
+    """C entry point ``fa_paged_decode_noalloc``: the paged decode without a workspace
+    (its partials go to the library's own per-device scratch); allocates nothing."""
+    if dtype is None:
+        dtype = _dtype_code(q.dtype)
+    st = load_library().fa_paged_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(out),
+        int(num_seqs), int(num_heads), int(num_kv_heads), int(head_size), int(block_size),
+        int(max_blocks_per_seq), int(max_context_len), float(scale), int(dtype), _stream(stream))
+    if st != 0:
+        raise FAError(st, "fa_paged_decode_noalloc")
 
 
 def _check_dev(name, t, dtype=None):

@@ -19,6 +19,9 @@ hipError_t decode_dispatch(const void *q, const void *kc, const void *vc, const 
                            int max_ctx, float scale, int dtype, void *workspace,
                            hipStream_t stream);
 size_t decode_workspace_bytes(int num_seqs, int num_heads, int max_context_len);
+hipError_t decode_noalloc_dispatch(const void *q, const void *kc, const void *vc, const int32_t *bt,
+                                   const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
+                                   int max_ctx, float scale, int dtype, hipStream_t stream);
 hipError_t bwd_dispatch(const void *q, const void *k, const void *v, const float *o,
                         const float *lse, const void *dout, float *dq, float *dk, float *dv, int B,
                         int H, int Hkv, int N, int d, float scale, int causal, int dtype,
@@ -428,6 +431,33 @@ extern "C" int fa_paged_decode(const void *q, const void *k_cache, const void *v
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+extern "C" int fa_paged_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                       const int32_t *block_tables, const int32_t *context_lens,
+                                       void *out, int num_seqs, int num_heads, int num_kv_heads,
+                                       int head_size, int block_size, int max_blocks_per_seq,
+                                       int max_context_len, float scale, int dtype, void *stream)
+{
+    size_t need = 0;
+    const int st = decode_args(q, k_cache, v_cache, block_tables, context_lens, out, num_seqs,
+                               num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                               max_context_len, scale, dtype, &need);
+    if (st != FA_OK) return st;
+    if (need > FA_DECODE_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    // the scratch is the current device's: the stream must belong to it
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (stream) {
+        int sdev = -1;
+        if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+        if (sdev != dev) return FA_ERR_INVALID_ARG;
+    }
+    const hipError_t e = fa::decode_noalloc_dispatch(q, k_cache, v_cache, block_tables, context_lens,
+                                                     out, num_seqs, num_heads, num_kv_heads,
+                                                     max_blocks_per_seq, max_context_len, scale,
+                                                     dtype, (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char *fa_strerror(int status)
 {
     switch (status) {
@@ -437,6 +467,7 @@ extern "C" const char *fa_strerror(int status)
     case FA_ERR_ALIGNMENT: return "misaligned pointer";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "HIP runtime error at launch";
+    case FA_ERR_SCRATCH: return "sizes need more than the no-allocation decode's scratch holds";
     default: return "unknown status";
     }
 }

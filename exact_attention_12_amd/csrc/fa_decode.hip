@@ -24,6 +24,8 @@
 #include "fa_device.h"
 #include "fa_tile.h"
 
+#include <atomic>
+
 namespace fa {
 
 constexpr int kDecD = 128;        // head size
@@ -567,6 +569,38 @@ static hipError_t launch_decode(const void *q, const void *kc, const void *vc, c
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of fa_paged_decode_noalloc: the per-partition partials go to this
+// file-scope device array instead of a caller's workspace.  Every GPU the
+// library runs on holds its own copy (loaded with the code object, kept until
+// the process ends).  In host code the name `scratch` is only a host-side
+// stand-in: the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current and kept in scratch_ptr[].
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+static std::atomic<void *> scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`.
+static hipError_t scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // two threads may both look it up the first time: same address
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 hipError_t decode_dispatch(const void *q, const void *kc, const void *vc, const int32_t *bt,
                            const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
                            int max_ctx, float scale, int dtype, void *workspace,
@@ -577,6 +611,21 @@ hipError_t decode_dispatch(const void *q, const void *kc, const void *vc, const 
                                        workspace, stream);
     return launch_decode<__bf16>(q, kc, vc, bt, cl, out, S, H, Hkv, MB, max_ctx, scale, workspace,
                                  stream);
+}
+
+// The paged decode with its partials in `scratch`.  Arguments validated by
+// the caller, including decode_workspace_bytes(S, H, max_ctx) <=
+// FA_DECODE_NOALLOC_SCRATCH_BYTES; `stream` belongs to the current device.
+// Nothing in the scratch needs clearing: the merge reads only partitions
+// below each context's end, which this call's partition kernel writes.
+hipError_t decode_noalloc_dispatch(const void *q, const void *kc, const void *vc, const int32_t *bt,
+                                   const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
+                                   int max_ctx, float scale, int dtype, hipStream_t stream)
+{
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    return decode_dispatch(q, kc, vc, bt, cl, out, S, H, Hkv, MB, max_ctx, scale, dtype, ws, stream);
 }
 
 }  // namespace fa

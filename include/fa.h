@@ -61,7 +61,9 @@ enum {
     FA_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head dim 96)     */
     FA_ERR_ALIGNMENT = -3,   /* a pointer is not aligned as documented           */
     FA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required       */
-    FA_ERR_HIP = -5          /* the HIP runtime refused a launch                 */
+    FA_ERR_HIP = -5,         /* the HIP runtime refused a launch                 */
+    FA_ERR_SCRATCH = -6      /* fa_paged_decode_noalloc: the sizes need more     */
+                             /* than FA_DECODE_NOALLOC_SCRATCH_BYTES of scratch  */
 };
 
 /*
@@ -381,6 +383,38 @@ int fa_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                     int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
                     int max_blocks_per_seq, int max_context_len, float scale, int dtype,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa_paged_decode_noalloc -- fa_paged_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and validation
+ * as fa_paged_decode, without the workspace: the per-partition partials go
+ * to a scratch array of FA_DECODE_NOALLOC_SCRATCH_BYTES that the library
+ * holds in each GPU's memory from its first use on that GPU until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine).
+ *   - Sizes whose workspace (fa_paged_decode_workspace_size) exceeds
+ *     FA_DECODE_NOALLOC_SCRATCH_BYTES return FA_ERR_SCRATCH and launch
+ *     nothing; 32 MiB holds num_seqs * num_heads *
+ *     ceil(max_context_len / 256) <= 64,000 partitions (e.g. 64 sequences x
+ *     32 heads at contexts up to 8,000 tokens).
+ *   - The scratch belongs to the device that is current when the call is
+ *     made; `stream` must belong to that device (else FA_ERR_INVALID_ARG).
+ *     Its address is looked up once per device (hipGetSymbolAddress), so the
+ *     first call on a device makes that HIP query before launching.
+ *   - Every call on one GPU shares that GPU's scratch, and a call leaves its
+ *     partials there: calls that overlap in time on one GPU (different
+ *     streams, or different threads, without ordering between them) race
+ *     and may return wrong results.  Calls ordered on one stream are safe.
+ *     Nothing in the scratch needs clearing between calls: a call reads
+ *     only partials it wrote itself.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int fa_paged_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens, void *out,
+                            int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                            int block_size, int max_blocks_per_seq, int max_context_len,
+                            float scale, int dtype, void *stream);
 
 /* fa_strerror -- a static, human-readable string for a status code. */
 const char *fa_strerror(int status);
