@@ -745,7 +745,11 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                 *(f32x4 *)(orow + d) = f32x4{acc[db][4 * r4 + 0] * inv, acc[db][4 * r4 + 1] * inv,
                                             acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv};
             }
-        if (h == 0) LSE[(int64_t)bh * N + qrow] = scale * m_ref + log2_hw(l_tot) * kLn2;
+        // a row with no visible key has m_ref = -inf: its lse is -inf, also at
+        // scale 0 (where scale * m_ref alone would give NaN)
+        if (h == 0)
+            LSE[(int64_t)bh * N + qrow] = (EXT != 0 && !(l_tot > 0.f)) ? -INFINITY
+                                                                       : scale * m_ref + log2_hw(l_tot) * kLn2;
     }
   }
 }

@@ -103,16 +103,19 @@ def test_deterministic(gpu, fa_lib):
 def check_sampled(cfg, dev, heads):
     """Whole backward pass at cfg's size on the device; the oracle on the
     kv-head groups in `heads` ((b, kv head) pairs), 256 sampled rows (dQ) and
-    256 sampled keys (dK, dV) each."""
+    256 sampled keys (dK, dV) of each group's own."""
     progress("fa_bwd sampled %s" % cfg.name)
     q, k, v = inputs.fwd_inputs(cfg)
     dout = inputs.bwd_dout(cfg)
     scale = float(np.float32(cfg.scale))
     dq, dk, dv = run_bwd(q, k, v, dout, scale, cfg.causal, dev)
-    rows = inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5)
-    keys = inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 8)
+    # rows and keys drawn independently for every (b, kv head) group,
+    # stratified over the 128-row tiles
+    all_rows = inputs.sample_rows_per_head(cfg.N, cfg.B * cfg.kv_heads, 256, seed=1000 * cfg.cid + 5)
+    all_keys = inputs.sample_rows_per_head(cfg.N, cfg.B * cfg.kv_heads, 256, seed=1000 * cfg.cid + 8)
     G = cfg.H // cfg.kv_heads
     for b, g in heads:
+        rows, keys = all_rows[b * cfg.kv_heads + g], all_keys[b * cfg.kv_heads + g]
         hs = slice(g * G, (g + 1) * G)
         sl = lambda t, s: t[b:b + 1, s].contiguous()
         ref = oracle.attention_bwd(sl(q, hs), sl(k, slice(g, g + 1)), sl(v, slice(g, g + 1)),

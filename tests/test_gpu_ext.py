@@ -19,7 +19,7 @@ import torch
 import exact_attention_12_amd as fa
 import oracle
 from exact_attention_12_amd import inputs
-from gpu_util import TOL, errors, progress
+from gpu_util import TOL, errors, gather_rows, oracle_per_head, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -61,10 +61,14 @@ def check(q, k, v, causal, window, mask, dev, label, rows=None, block_map=False)
         progress("%s map vs no map: max|dO|=%.3g max|dlse|=%.3g" % (label, dmax, lmax))
         assert dmax <= MAP_DIFF and lmax <= MAP_DIFF, (label, dmax, lmax)
     torch.cuda.synchronize()
-    ro, rl = oracle.attention_ext(q, k, v, scale, causal, window, mask, rows=rows)
     og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
-    if rows is not None:
-        og, lg = og[:, :, rows], lg[:, :, rows]
+    if rows is None:
+        ro, rl = oracle.attention_ext(q, k, v, scale, causal, window, mask)
+    else:
+        # rows [B * H, R]: each head's own sampled rows; the mask here is one
+        # [Nq, Nk] matrix broadcast over batch and heads
+        ro, rl = oracle_per_head(oracle.attention_ext, q, k, v, rows, scale, causal, window, mask)
+        og, lg = gather_rows(og, rows), gather_rows(lg, rows)
     empty = np.isneginf(rl)
     assert np.all(og[empty] == 0) and np.all(np.isneginf(lg[empty])), label
     ok = ~empty
@@ -133,7 +137,7 @@ def test_tril_mask_equals_causal(gpu, fa_lib):
 def test_headline_sliding_window_sampled(gpu, fa_lib):
     cfg = inputs.FWD_CAUSAL_N8192
     q, k, v = inputs.fwd_inputs(cfg)
-    rows = inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5)
+    rows = inputs.sample_rows_per_head(cfg.N, cfg.B * cfg.H, 256, seed=1000 * cfg.cid + 5)
     check(q, k, v, True, (1024, -1), None, gpu, "B2 H32 N8192 window 1024", rows=rows)
 
 
@@ -145,8 +149,35 @@ def test_headline_boolean_mask_sampled(gpu, fa_lib):
     keep = torch.from_numpy(np.random.default_rng(64).random((N // 128, N // 64)) < 0.5)
     m = keep.repeat_interleave(128, 0).repeat_interleave(64, 1) & torch.ones(N, N, dtype=torch.bool).tril()
     m[:, 0] = True
-    rows = inputs.sample_rows(N, 256, seed=1000 * cfg.cid + 5)
+    rows = inputs.sample_rows_per_head(N, cfg.B * cfg.H, 256, seed=1000 * cfg.cid + 5)
     check(q, k, v, False, (-1, -1), m, gpu, "B2 H32 N8192 block-sparse mask", rows=rows)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("use_map", [False, True])
+def test_zero_scale_rows_without_keys(gpu, fa_lib, dt, use_map):
+    # scale 0: every visible key has probability 1/n, so o is the mean of the
+    # visible values and lse = ln n; rows that see no key (fully masked rows,
+    # and the first Nq - Nk rows of a bottom-right causal rectangle) must
+    # still give o = 0 and lse = -inf exactly, not NaN from 0 * (-inf)
+    Nq, Nk = 300, 200
+    d = 128 if dt == "bf16" else 64
+    q, k, v = ext_inputs(67, 1, 2, 2, Nq, Nk, d, DT[dt])
+    m = torch.from_numpy(np.random.default_rng(68).random((Nq, Nk)) < 0.6)
+    m[150:160] = False
+    progress("fa_fwd_ext scale 0 %s map=%d" % (dt, use_map))
+    o, lse = fa.forward_ext(q.to(gpu), k.to(gpu), v.to(gpu), scale=0.0, causal=True, mask=m.to(gpu),
+                            block_map=True if use_map else None)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_ext(q, k, v, 0.0, True, (-1, -1), m)
+    og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    empty = np.isneginf(rl)
+    assert empty[:, :, :100].all() and empty[:, :, 150:160].all()
+    assert not np.isnan(lg).any(), "NaN lse"
+    assert np.all(og[empty] == 0) and np.all(np.isneginf(lg[empty]))
+    tol = TOL[q.dtype]
+    assert np.abs(og[~empty] - ro[~empty]).max() <= tol["o_max"]
+    assert np.abs(lg[~empty] - rl[~empty]).max() <= tol["lse_max"]
 
 
 # ---- block map of the mask --------------------------------------------------
@@ -241,6 +272,6 @@ def test_headline_block_sparse_mask_with_map_sampled(gpu, fa_lib):
     keep = torch.from_numpy(np.random.default_rng(64).random((N // 128, N // 64)) < 0.5)
     m = keep.repeat_interleave(128, 0).repeat_interleave(64, 1) & torch.ones(N, N, dtype=torch.bool).tril()
     m[:, 0] = True
-    rows = inputs.sample_rows(N, 256, seed=1000 * cfg.cid + 5)
+    rows = inputs.sample_rows_per_head(N, cfg.B * cfg.H, 256, seed=1000 * cfg.cid + 5)
     check(q, k, v, False, (-1, -1), m, gpu, "B2 H32 N8192 block-sparse mask, map", rows=rows,
           block_map=True)

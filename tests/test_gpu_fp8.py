@@ -13,7 +13,7 @@ import torch
 import exact_attention_12_amd as fa
 import oracle
 from exact_attention_12_amd import inputs
-from gpu_util import FP8_TOL, errors, progress
+from gpu_util import FP8_TOL, errors, gather_rows, oracle_per_head, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -69,12 +69,16 @@ def run_fp8(cfg, dev, rows=None, label=""):
     for t, layout in ((q, 0), (k, 0), (v, 1)):
         c, e = oracle.quant_fp8(t, layout)
         deq.append(torch.from_numpy(oracle.dequant_fp8(c, e, t.shape[0], t.shape[1], N, d, layout)))
-    o_ref, l_ref = oracle.attention(deq[0], deq[1], deq[2], scale, cfg.causal, rows=rows)
-    o_abs, _ = oracle.attention(deq[0], deq[1], deq[2].abs(), scale, cfg.causal, rows=rows)
+    if rows is None:
+        o_ref, l_ref = oracle.attention(deq[0], deq[1], deq[2], scale, cfg.causal)
+        o_abs, _ = oracle.attention(deq[0], deq[1], deq[2].abs(), scale, cfg.causal)
+    else:  # rows [B * H, R]: each head's own rows
+        o_ref, l_ref = oracle_per_head(oracle.attention, deq[0], deq[1], deq[2], rows, scale, cfg.causal)
+        o_abs, _ = oracle_per_head(oracle.attention, deq[0], deq[1], deq[2].abs(), rows, scale, cfg.causal)
     bound = FP8_TOL["rel"] * o_abs + FP8_TOL["abs"]
     og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
     if rows is not None:
-        og, lg = og[:, :, rows], lg[:, :, rows]
+        og, lg = gather_rows(og, rows), gather_rows(lg, rows)
     assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
     omax, omean = errors(og, o_ref)
     lmax, _ = errors(lg, l_ref)
@@ -103,4 +107,5 @@ def test_fwd_fp8_deterministic(gpu, fa_lib):
 
 def test_fwd_fp8_headline_sampled(gpu, fa_lib):
     cfg = inputs.FWD_CAUSAL_N8192
-    run_fp8(cfg, gpu, rows=inputs.sample_rows(cfg.N, 256, seed=1000 * cfg.cid + 5), label=cfg.name)
+    run_fp8(cfg, gpu, rows=inputs.sample_rows_per_head(cfg.N, cfg.B * cfg.H, 256, seed=1000 * cfg.cid + 5),
+            label=cfg.name)
