@@ -20,8 +20,13 @@
 // instruction v_mfma_f32_32x32x64_f8f6f4 (64-deep contraction, 32 bytes per
 // lane):
 //  - S^T = K Q^T with Q rows in registers and K tiles (64 keys) in LDS;
-//    raw dot products of the codes are exact in the fp32 accumulator and are
-//    scaled by scale * 2^(e_q + e_k) per tile;
+//    the raw dot products of the codes are scaled by scale * 2^(e_q + e_k)
+//    per tile.  The matrix instruction sums its products in groups of 8 along
+//    the contraction, and inside a group drops the bits of a product below
+//    about 2^-13 of the group's largest one (measured: 256 + 7 x 2^-6 gives
+//    256); across groups it accumulates in fp32.  Scores are therefore exact
+//    only when the products of a group are within ~2^13 of each other, as
+//    they are for data without a dominant head dimension;
 //  - the rows of each K tile are permuted as they land in LDS, so that the
 //    accumulator register r of block kb in lane half h holds key
 //    32 h + 16 kb + r of the tile.  The 32 probabilities a lane packs (one
@@ -29,8 +34,10 @@
 //    run of bytes the lane reads from a row of the d-major V tile: the P.V
 //    operands need no transpose and no shuffle;
 //  - P~ = 2^(s c - m_ref) is rounded to E4M3 for the P.V product.  The V
-//    block scales are folded into the exponent (P~ 2^(e_v - e_vmax), exact
-//    powers of two) and the output is multiplied by 2^e_vmax at the end;
+//    block scale enters that product through the instruction's E8M0 scale
+//    operand as 2^(e_v - e_vmax) (exact, and P~ keeps its own precision
+//    whatever the V block's magnitude); the output is multiplied by 2^e_vmax
+//    at the end;
 //  - the lazy reference max of the bf16 forward, with the bound on P~ at 2^8
 //    so that every probability is a finite E4M3 value; O = acc / l with l
 //    the fp32 sum of the unrounded probabilities; lse = m + ln l.
@@ -320,7 +327,11 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
             const char *Ks = smem + STAGE * STAGEB;
             const char *Vs = Ks + KTILEB;
             const float c = ldexpf(cq, ke_next);
-            const int vsh = ve_next - evmax;  // <= 0: V block scale relative to the largest
+            // V block scale relative to the largest, <= 0; applied to the V
+            // operand of the P.V product through the instruction's E8M0
+            // scale (2^(x - 127)).  A block more than 2^127 below the largest
+            // contributes nothing (no E8M0 value represents its scale).
+            const int vsh = ve_next - evmax;
 
             // S^T = K Q^T: lane (col = query, h), register r of block kb holds
             // tile key 32h + 16kb + r
@@ -372,9 +383,9 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
                 for (int db = 0; db < DB; ++db) acc[db] *= alpha;
                 mref = msafe;
             };
-            // P' = P~ 2^vsh = 2^(s c - mref + vsh); returns this lane's sum of P'
+            // P~ = 2^(s c - mref); returns this lane's sum
             auto exponentiate = [&](f32x16 (&p)[2]) __attribute__((always_inline)) {
-                const float sub = mref - (float)vsh;
+                const float sub = mref;
                 float part[4];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -388,14 +399,13 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
             f32x16 p[2];
             if (j == 0) rebase();
             float rs = exponentiate(p);
-            // the bound applies to the unshifted P~ = P' 2^-vsh
-            if (j != 0 && __builtin_amdgcn_ballot_w64(!(ldexpf(rs, -vsh) <= kPMax)) != 0) {
+            if (j != 0 && __builtin_amdgcn_ballot_w64(!(rs <= kPMax)) != 0) {
                 rebase();
                 rs = exponentiate(p);
             }
-            l_run += ldexpf(rs, -vsh);
+            l_run += rs;
 
-            // P' as E4M3: byte 16kb + r of the lane's 32 is register r of block kb
+            // P~ as E4M3: byte 16kb + r of the lane's 32 is register r of block kb
             // (the first conversion of a word writes its low half and the
             // second its high half, so the word's prior contents never show)
             i32x8 pb;
@@ -408,17 +418,20 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
                     const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][4 * w], p[kb][4 * w + 1], undef_word, false);
                     pb[4 * kb + w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][4 * w + 2], p[kb][4 * w + 3], lo, true);
                 }
-            // O^T += V^T P'^T: lane (col = d row of the block, h) reads bytes
-            // 32h .. 32h+31 of its V tile row: keys 32h .. 32h+31
-            __builtin_amdgcn_s_setprio(1);
+            // O^T += 2^vsh V^T P~^T: lane (col = d row of the block, h) reads
+            // bytes 32h .. 32h+31 of its V tile row: keys 32h .. 32h+31
+            if (vsh >= -127) {
+                const int vscale = 127 + vsh;  // E8M0 code of 2^vsh
+                __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const u32x4 a0 = *(const u32x4 *)(Vs + v_rd[db][0]);
-                const u32x4 a1 = *(const u32x4 *)(Vs + v_rd[db][1]);
-                const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, acc[db], 0, 0, 0, 0, 0, 0);
+                for (int db = 0; db < DB; ++db) {
+                    const u32x4 a0 = *(const u32x4 *)(Vs + v_rd[db][0]);
+                    const u32x4 a1 = *(const u32x4 *)(Vs + v_rd[db][1]);
+                    const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, acc[db], 0, 0, 0, vscale, 0, 127);
+                }
+                __builtin_amdgcn_s_setprio(0);
             }
-            __builtin_amdgcn_s_setprio(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         };

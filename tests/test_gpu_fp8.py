@@ -109,3 +109,33 @@ def test_fwd_fp8_headline_sampled(gpu, fa_lib):
     cfg = inputs.FWD_CAUSAL_N8192
     run_fp8(cfg, gpu, rows=inputs.sample_rows_per_head(cfg.N, cfg.B * cfg.H, 256, seed=1000 * cfg.cid + 5),
             label=cfg.name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_uneven_v_block_scales(gpu, fa_lib, causal):
+    # V blocks (128 rows) at magnitudes 2^8, 1, 2^-6, 2^3, 1: the block
+    # exponents differ by up to 14 binades, so probabilities of the small
+    # blocks must not be rounded relative to the largest block's scale
+    cfg = inputs.FwdConfig(72, 1, 2, 600, 128, torch.bfloat16, causal, 1.0, "")
+    q, k, v = inputs.fwd_inputs(cfg)
+    f = torch.tensor([2.0 ** 8, 1.0, 2.0 ** -6, 2.0 ** 3, 1.0]).repeat_interleave(128)[:cfg.N]
+    v = (v.float() * f[None, None, :, None]).to(cfg.dtype)
+    B, H, N, d = q.shape
+    scale = float(np.float32(cfg.scale))
+    progress("fa_fwd_fp8 uneven V block scales causal=%d" % causal)
+    q8, qe = fa.quant_fp8(q.to(gpu), 0)
+    k8, ke = fa.quant_fp8(k.to(gpu), 0)
+    v8, ve = fa.quant_fp8(v.to(gpu), 1)
+    o, lse = fa.forward_fp8(q8, k8, v8, qe, ke, ve, B, H, H, N, d, scale, causal)
+    torch.cuda.synchronize()
+    deq = []
+    for t, layout in ((q, 0), (k, 0), (v, 1)):
+        c, e = oracle.quant_fp8(t, layout)
+        deq.append(torch.from_numpy(oracle.dequant_fp8(c, e, B, H, N, d, layout)))
+    o_ref, l_ref = oracle.attention(deq[0], deq[1], deq[2], scale, causal)
+    o_abs, _ = oracle.attention(deq[0], deq[1], deq[2].abs(), scale, causal)
+    og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    ratio = float((np.abs(og - o_ref) / (FP8_TOL["rel"] * o_abs + FP8_TOL["abs"])).max())
+    lmax = float(np.abs(lg - l_ref).max())
+    progress("uneven V scales causal=%d max |dO|/bound=%.3f max|dlse|=%.3g" % (causal, ratio, lmax))
+    assert ratio <= 1.0 and lmax <= FP8_TOL["lse_max"], (ratio, lmax)
