@@ -334,19 +334,70 @@ static double or_score(const double *q, const double *k, int N, int d, double sc
 }
 
 /*
- * FlashAttention-1 loop order ([YJ] 5.2 pseudocode; [SD] "main loop"):
- * outer loop over K/V tiles j, inner loop over Q tiles i; O, l, m live in
- * "HBM" arrays (here: o, l, m) initialised to 0, 0, -inf and are read and
- * written back on every (i, j) step.  Per step, with the tile's own
- * statistics m~ = rowmax(S_ij), P~ = exp(S_ij - m~), l~ = rowsum(P~):
- *     m_new = max(m, m~)
- *     l_new = e^(m - m_new) l + e^(m~ - m_new) l~
- *     O     = (l e^(m - m_new) O + e^(m~ - m_new) P~ V_j) / l_new
- * The O update is the merge of two normalised partial results, [SU] Eq. (4);
- * the printed pseudocode's inverse on the exponential factors is read as a
- * typesetting slip, since Eq. (4) and [YJ] 6.2 carry no inverse.
- * A tile row with no admissible key leaves that row's state unchanged.
- * Outputs o [N, d] and lse [N] (lse = m + ln l).
+ * [SU] Eq. (4): two partial results of one row over disjoint sets of keys,
+ * each normalised by its own sum, (m1, l1, o1) and (m2, l2, o2), combine into
+ * the result over the union:
+ *     m = max(m1, m2),  w1 = l1 e^(m1 - m),  w2 = l2 e^(m2 - m),
+ *     l = w1 + w2,      o = (w1 o1 + w2 o2) / l.
+ * A part with l = 0 (no admissible key) has weight 0.  Part 1 is
+ * overwritten with the result.
+ */
+static void or_merge_partial(double *m1, double *l1, double *o1, double m2, double l2,
+                             const double *o2, int d)
+{
+    if (!(l2 > 0.0)) return;
+    if (!(*l1 > 0.0)) {
+        *m1 = m2;
+        *l1 = l2;
+        for (int c = 0; c < d; ++c) o1[c] = o2[c];
+        return;
+    }
+    double m = *m1 > m2 ? *m1 : m2;
+    double w1 = *l1 * exp(*m1 - m), w2 = l2 * exp(m2 - m);
+    double l = w1 + w2;
+    for (int c = 0; c < d; ++c) o1[c] = (w1 * o1[c] + w2 * o2[c]) / l;
+    *m1 = m;
+    *l1 = l;
+}
+
+/*
+ * The partial result of query row i over the keys of one key tile,
+ * [j0, j0 + Bc) ([SU] Eq. (1) restricted to those keys): its max m~, sum
+ * l~ = sum_j exp(s_ij - m~) and normalised output o~ = sum_j exp(s_ij - m~)
+ * v_j / l~.  Returns l~ (0 when no key of the tile is admissible); s is
+ * scratch of Bc doubles.
+ */
+static double or_tile_partial(const double *q, const double *k, const double *v, int N, int d,
+                              double scale, int causal, int64_t i, int64_t j0, int Bc, double *s,
+                              double *mt, double *ot)
+{
+    double m = -INFINITY;
+    for (int cc = 0; cc < Bc; ++cc) {
+        s[cc] = or_score(q, k, N, d, scale, causal, i, j0 + cc);
+        if (s[cc] > m) m = s[cc];
+    }
+    *mt = m;
+    if (m == -INFINITY) return 0.0;
+    double l = 0.0;
+    for (int cc = 0; cc < Bc; ++cc) l += exp(s[cc] - m); /* exp(-inf) = 0: masked keys */
+    for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int cc = 0; cc < Bc; ++cc)
+            if (j0 + cc < N) acc += exp(s[cc] - m) * v[(j0 + cc) * d + c];
+        ot[c] = acc / l;
+    }
+    return l;
+}
+
+/*
+ * FlashAttention-1 loop order ([YJ] 5.2): the outer loop runs over the K/V
+ * tiles j, the inner loops over the Q tiles of Br rows and their rows; the
+ * running state (m, l, O) of every row lives outside the loops (in HBM, on
+ * the page) and absorbs each tile's partial result through the merge of
+ * [SU] Eq. (4).  (The [YJ] 5.2 pseudocode writes an inverse on the
+ * exponential factors of that update; Eq. (4) and [YJ] 6.2 have none, so it
+ * is read as a typesetting slip.)  Outputs o [N, d] and lse [N] (lse =
+ * m + ln l).
  */
 int oracle_tiled_fa1(const double *q, const double *k, const double *v, int N, int d, double scale,
                      int causal, int Br, int Bc, double *o, double *lse)
@@ -354,49 +405,25 @@ int oracle_tiled_fa1(const double *q, const double *k, const double *v, int N, i
     if (!q || !k || !v || !o || !lse || N < 1 || d < 1 || Br < 1 || Bc < 1) return -1;
     double *m = (double *)malloc(sizeof(double) * N);
     double *l = (double *)malloc(sizeof(double) * N);
-    double *pt = (double *)malloc(sizeof(double) * Bc);
-    if (!m || !l || !pt) { free(m); free(l); free(pt); return -1; }
+    double *s = (double *)malloc(sizeof(double) * Bc);
+    double *ot = (double *)malloc(sizeof(double) * d);
+    if (!m || !l || !s || !ot) { free(m); free(l); free(s); free(ot); return -1; }
     for (int64_t i = 0; i < N; ++i) {
         m[i] = -INFINITY;
         l[i] = 0.0;
         for (int c = 0; c < d; ++c) o[i * d + c] = 0.0;
     }
     int Tr = (N + Br - 1) / Br, Tc = (N + Bc - 1) / Bc;
-    for (int j = 0; j < Tc; ++j) {
-        for (int it = 0; it < Tr; ++it) {
-            for (int r = 0; r < Br; ++r) {
+    for (int j = 0; j < Tc; ++j)
+        for (int it = 0; it < Tr; ++it)
+            for (int r = 0; r < Br && (int64_t)it * Br + r < N; ++r) {
                 int64_t i = (int64_t)it * Br + r;
-                if (i >= N) break;
-                double mt = -INFINITY;
-                for (int cc = 0; cc < Bc; ++cc) {
-                    pt[cc] = or_score(q, k, N, d, scale, causal, i, (int64_t)j * Bc + cc);
-                    if (pt[cc] > mt) mt = pt[cc];
-                }
-                if (mt == -INFINITY) continue; /* nothing admissible in this tile */
-                double lt = 0.0;
-                for (int cc = 0; cc < Bc; ++cc) {
-                    pt[cc] = exp(pt[cc] - mt); /* exp(-inf) = 0 for masked keys */
-                    lt += pt[cc];
-                }
-                double mnew = m[i] > mt ? m[i] : mt;
-                double a_old = exp(m[i] - mnew); /* 0 when m[i] = -inf */
-                double a_new = exp(mt - mnew);
-                double lnew = a_old * l[i] + a_new * lt;
-                for (int c = 0; c < d; ++c) {
-                    double pv = 0.0;
-                    for (int cc = 0; cc < Bc; ++cc) {
-                        int64_t jj = (int64_t)j * Bc + cc;
-                        if (jj < N) pv += pt[cc] * v[jj * d + c];
-                    }
-                    o[i * d + c] = (l[i] * a_old * o[i * d + c] + a_new * pv) / lnew;
-                }
-                m[i] = mnew;
-                l[i] = lnew;
+                double mt;
+                double lt = or_tile_partial(q, k, v, N, d, scale, causal, i, (int64_t)j * Bc, Bc, s, &mt, ot);
+                or_merge_partial(&m[i], &l[i], o + i * d, mt, lt, ot, d);
             }
-        }
-    }
     for (int64_t i = 0; i < N; ++i) lse[i] = l[i] > 0.0 ? m[i] + log(l[i]) : -INFINITY;
-    free(m); free(l); free(pt);
+    free(m); free(l); free(s); free(ot);
     return 0;
 }
 

@@ -71,9 +71,9 @@ MUTATIONS = [
     ("fp16_exponent_bias",
      "mag = ldexp((double)(1024 + f), e - 25);",
      "mag = ldexp((double)(1024 + f), e - 24);"),
-    ("tiled_fa1_rescale_sign",
-     "double a_old = exp(m[i] - mnew);",
-     "double a_old = exp(mnew - m[i]);"),
+    ("tiled_fa1_merge_sign",
+     "double w1 = *l1 * exp(*m1 - m), w2 = l2 * exp(m2 - m);",
+     "double w1 = *l1 * exp(m - *m1), w2 = l2 * exp(m2 - m);"),
     ("tiled_fa2_rescale_sign",
      "double alpha = exp(m - mnew);",
      "double alpha = exp(mnew - m);"),
