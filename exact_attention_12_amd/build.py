@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_decode.hip", "fa_capi.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip",
+                                                    "fa_decode.hip", "fa_capi.cpp")]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU
 # instructions; hipcc's host pass warns that it does not know the feature.
@@ -27,22 +28,43 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libfa.so (always recompiles) and return its path."""
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + SOURCES + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _compile(hipcc, src, obj):
+    """One translation unit to a position-independent object; returns (src, rc, messages)."""
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    res = subprocess.run([hipcc] + flags + ["-c", src, "-o", obj], capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, "\n".join(msgs)))
-    if verbose and msgs:
-        print("\n".join(msgs), flush=True)
+    return src, res.returncode, msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libfa.so (always recompiles; one process per source file) and return its path."""
+    import concurrent.futures
+    import shutil
+    import tempfile
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmpdir = tempfile.mkdtemp(prefix="fa_build_")
+    try:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in SOURCES]
+        if verbose:
+            print(" ".join([hipcc] + HIPCC_FLAGS + ["-c"] + SOURCES), flush=True)
+        workers = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(lambda so: _compile(hipcc, *so), zip(SOURCES, objs)))
+        for src, rc, msgs in results:
+            if rc != 0:
+                raise RuntimeError("hipcc failed on %s (%d):\n%s" % (src, rc, "\n".join(msgs)))
+            if verbose and msgs:
+                print("\n".join(msgs), flush=True)
+        tmp = LIB + ".tmp%d" % os.getpid()
+        res = subprocess.run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            if os.path.exists(tmp):
+                os.remove(tmp)
+            raise RuntimeError("link failed (%d):\n%s" % (res.returncode, res.stdout + res.stderr))
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     # the library must load with every symbol resolved (a kernel whose host
     # launch stub was not emitted shows up here, not at the first call)
     chk = subprocess.run([sys.executable, "-c", "import ctypes, sys; ctypes.CDLL(sys.argv[1])", tmp],

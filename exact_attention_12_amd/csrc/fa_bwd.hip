@@ -42,6 +42,7 @@
 // Causal: workgroups take a heavy and a light block of the same head, blocks
 // entirely on the masked side of the diagonal are skipped, and only blocks
 // that straddle it (or the ragged tail) pay for element masks.
+#include "fa_sizes.h"
 #include "fa_tile.h"
 
 #include <climits>
@@ -727,11 +728,7 @@ void fa_bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-size_t bwd_workspace_bytes(int B, int H, int N)
-{
-    const size_t rows = (size_t)B * H * N;
-    return ((2 * rows * sizeof(float)) + 255) / 256 * 256;
-}
+// (bwd_workspace_bytes, the workspace size, is in fa_sizes.h)
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *o,

@@ -3,6 +3,7 @@
 // Validation runs before any HIP call, so an invalid call launches nothing
 // and writes nothing.
 #include "fa.h"
+#include "fa_sizes.h"
 
 #include <hip/hip_runtime.h>
 
@@ -18,7 +19,6 @@ hipError_t decode_dispatch(const void *q, const void *kc, const void *vc, const 
                            const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
                            int max_ctx, float scale, int dtype, void *workspace,
                            hipStream_t stream);
-size_t decode_workspace_bytes(int num_seqs, int num_heads, int max_context_len);
 hipError_t decode_noalloc_dispatch(const void *q, const void *kc, const void *vc, const int32_t *bt,
                                    const int32_t *cl, void *out, int S, int H, int Hkv, int MB,
                                    int max_ctx, float scale, int dtype, hipStream_t stream);
@@ -26,12 +26,10 @@ hipError_t bwd_dispatch(const void *q, const void *k, const void *v, const float
                         const float *lse, const void *dout, float *dq, float *dk, float *dv, int B,
                         int H, int Hkv, int N, int d, float scale, int causal, int dtype,
                         void *workspace, hipStream_t stream);
-size_t bwd_workspace_bytes(int B, int H, int N);
 hipError_t fwd_ext_dispatch(const void *q, const void *k, const void *v, float *o, float *lse, int B,
                             int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int wl,
                             int wr, const uint8_t *mask, int64_t msb, int64_t msh, int ldm,
                             const uint32_t *blocks, int dtype, hipStream_t stream);
-size_t mask_blocks_words(int B, int H, int Nq, int Nk, int64_t msb, int64_t msh);
 hipError_t fwd_paged_dispatch(const void *q, const void *kc, const void *vc, const int32_t *tables,
                               const int32_t *ctx_lens, float *o, float *lse, int S, int H, int Hkv,
                               int Nq, int mbps, uint64_t cache_bytes, float scale, int causal,

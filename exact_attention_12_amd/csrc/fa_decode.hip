@@ -22,6 +22,7 @@
 //    sums combine across the lane pair and then across waves through LDS.
 #include "fa.h"
 #include "fa_device.h"
+#include "fa_sizes.h"
 #include "fa_tile.h"
 
 #include <atomic>
@@ -514,14 +515,6 @@ void fa_decode_merge_kernel(const int32_t *__restrict__ context_lens, T *__restr
     T *orow = out + (int64_t)r * kDecD + 2 * lane;
     orow[0] = f32_to_elem<T>(o0 * inv);
     orow[1] = f32_to_elem<T>(o1 * inv);
-}
-
-size_t decode_workspace_bytes(int num_seqs, int num_heads, int max_context_len)
-{
-    const int64_t np = (max_context_len + kDecPart - 1) / kDecPart;
-    const int64_t parts = (int64_t)num_seqs * num_heads * (np > 0 ? np : 1);
-    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
-    return (size_t)(up(parts * kDecD * 4) + 2 * up(parts * 4));
 }
 
 template <typename T>

@@ -36,6 +36,7 @@
 //  - causal: tiles entirely above the diagonal are never loaded; a wave skips
 //    the arithmetic of tiles that are fully masked for its 32 rows; only
 //    diagonal and ragged-tail tiles pay for element masks.
+#include "fa_sizes.h"
 #include "fa_tile.h"
 
 #include <type_traits>
@@ -817,25 +818,7 @@ hipError_t fwd_dispatch(const void *q, const void *k, const void *v, float *o, f
     }
 }
 
-// Shape of the block map of a mask (see FwdExt::blocks): query blocks of
-// kMapRows rows, key blocks of kMapCols keys, 32 key blocks per word; the
-// map of slice (b, h) is shared along a dimension the mask broadcasts over.
-constexpr int kMapRows = 128, kMapCols = 64;
-struct MapShape {
-    int nqb, nkw, Bs, Hs;
-    int64_t bmb, bmh;  // word strides between batches and heads (0: broadcast)
-};
-MapShape map_shape(int B, int H, int Nq, int Nk, int64_t msb, int64_t msh)
-{
-    MapShape m;
-    m.nqb = (Nq + kMapRows - 1) / kMapRows;
-    m.nkw = ((Nk + kMapCols - 1) / kMapCols + 31) / 32;
-    m.Bs = msb ? B : 1;
-    m.Hs = msh ? H : 1;
-    m.bmh = msh ? (int64_t)m.nqb * 2 * m.nkw : 0;
-    m.bmb = msb ? (int64_t)m.Hs * m.nqb * 2 * m.nkw : 0;
-    return m;
-}
+// (map_shape, the block map's shape, is in fa_sizes.h)
 
 // x has a zero byte
 __device__ __forceinline__ bool zero_byte(uint32_t x) { return ((x - 0x01010101u) & ~x & 0x80808080u) != 0; }
@@ -906,12 +889,6 @@ void fa_mask_blocks_kernel(const uint8_t *__restrict__ mask, int Hs, int Nq, int
         out[w] = a;
         out[nkw + w] = f & a;
     }
-}
-
-size_t mask_blocks_words(int B, int H, int Nq, int Nk, int64_t msb, int64_t msh)
-{
-    const MapShape m = map_shape(B, H, Nq, Nk, msb, msh);
-    return (size_t)m.Bs * m.Hs * m.nqb * 2 * m.nkw;
 }
 
 // Arguments validated by the caller (the mask as for fwd_ext_dispatch; the
