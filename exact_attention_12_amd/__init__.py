@@ -62,7 +62,12 @@ def load_library():
         raise RuntimeError(
             "libfa.so is not built (expected at %s); build it with "
             "`python -m exact_attention_12_amd.build`" % path)
-    lib = ctypes.CDLL(path)
+    _LIB = _bind(ctypes.CDLL(path))
+    return _LIB
+
+
+def _bind(lib):
+    """Declare the argument and result types of every entry point on a loaded library."""
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_fwd.restype = i
@@ -96,7 +101,6 @@ def load_library():
     lib.fa_paged_decode_noalloc.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
-    _LIB = lib
     return lib
 
 

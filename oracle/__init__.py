@@ -45,10 +45,14 @@ _CODES = {torch.float32: OR_F32, torch.bfloat16: OR_BF16, torch.float16: OR_F16,
 
 
 def build() -> str:
-    """Compile liboracle.so with gcc (no -ffast-math) and return its path."""
+    """Compile liboracle.so with gcc (no -ffast-math) and return its path.
+
+    ORACLE_EXTRA_CFLAGS (space-separated) adds flags, e.g. the sanitizer
+    build of the host-sanitizer test."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra",
-           SRC, "-o", tmp, "-lm"]
+    extra = os.environ.get("ORACLE_EXTRA_CFLAGS", "").split()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra"] + extra + \
+          [SRC, "-o", tmp, "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + res.stdout + res.stderr)

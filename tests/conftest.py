@@ -14,8 +14,17 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def fa_lib():
-    """libfa.so loaded through the binding (built first only if absent)."""
+    """libfa.so loaded through the binding (built first only if absent).
+
+    FA_HOST_CAPI_LIB names another build of the C ABI to bind instead: the
+    host-only sanitizer build of tests/test_host_sanitizers.py, for the host
+    validation tests (it launches nothing)."""
     import exact_attention_12_amd as fa
+    alt = os.environ.get("FA_HOST_CAPI_LIB")
+    if alt:
+        import ctypes
+        fa._LIB = fa._bind(ctypes.CDLL(alt))
+        return fa._LIB
     if not os.path.exists(fa.lib_path()):
         from exact_attention_12_amd import build
         build.build()
