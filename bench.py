@@ -48,6 +48,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak (published)
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (published)
+PEAK_CLOCK_GHZ = 2.4       # the shader clock the published peaks assume
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
@@ -73,6 +74,87 @@ def measured_traffic(kernel, src_hash):
     if not rec or rec.get("source_hash") != src_hash:
         return None
     return rec.get("bytes_per_launch")
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _sclk_sources():
+    """sysfs files that report the GPU's current shader clock: pp_dpm_sclk, whose
+    starred line is the current frequency."""
+    import glob
+    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+
+
+def _read_sclk_ghz(path):
+    with open(path) as fh:
+        for line in fh:
+            if line.rstrip().endswith("*"):
+                mhz = line.split(":", 1)[1].strip().rstrip("*").strip()
+                return float(mhz.lower().replace("mhz", "")) / 1e3
+    return None
+
+
+class ClockSampler:
+    """Samples the GPU shader clock from sysfs every few milliseconds on a host
+    thread while the GPU runs; reports the median in GHz (None if unreadable).
+    With several cards visible, the one whose clock moves most is taken."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+        self.period = period_s
+        self.files = _sclk_sources()
+        self.samples = {f: [] for f in self.files}
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            for f in self.files:
+                try:
+                    g = _read_sclk_ghz(f)
+                except (OSError, ValueError, IndexError):
+                    g = None
+                if g is not None:
+                    self.samples[f].append(g)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.files:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.files:
+            self._stop.set()
+            self._t.join()
+
+    def result(self):
+        best = None
+        for f, xs in self.samples.items():
+            if len(xs) >= 5:
+                spread = max(xs) - min(xs)
+                if best is None or spread > best[0]:
+                    best = (spread, f, xs)
+        if best is None:
+            return None
+        xs = best[2]
+        return dict(ghz_median=round(median(xs), 3), ghz_min=round(min(xs), 3), ghz_max=round(max(xs), 3),
+                    samples=len(xs), source=best[1])
 
 
 def cpu_baseline(q, k, v, scale, causal, target_s=12.0):
@@ -102,9 +184,32 @@ def cpu_baseline(q, k, v, scale, causal, target_s=12.0):
     nh = int(min(H, max(1, round(target_s / max(dt * full_head / fl, 1e-3)))))
     dt, fl = run(nh, None)
     return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                seconds=round(dt, 3),
+                seconds=round(dt, 3), cpu_model=cpu_model(),
                 sample="fp64 oracle on heads 0..%d of batch 0 of the forward workload "
                        "(all %d query rows each, causal): %.3g flop" % (nh - 1, N, fl))
+
+
+def cpu_long_context_sample(rows_per_head=256):
+    """The oracle on the long-context forward workload (B=1 H=8 N=65536 d=128
+    causal): rows_per_head sampled rows of every head, and the full problem
+    extrapolated from them by the ratio of per-row work sum(i + 1)."""
+    import numpy as np
+    import oracle
+    from exact_attention_12_amd import inputs
+    cfg = inputs.FWD_CAUSAL_N65536
+    q, k, v = inputs.fwd_inputs(cfg)
+    threads = oracle.default_threads()
+    rows = inputs.sample_rows(cfg.N, rows_per_head, seed=1000 * cfg.cid + 5)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, float(np.float32(cfg.scale)), True, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    work_sample = float((rows + 1).sum())
+    work_full = cfg.N * (cfg.N + 1) / 2.0
+    flop = 4.0 * cfg.d * work_sample * cfg.B * cfg.H
+    return dict(workload=cfg.name, rows_per_head=rows_per_head, heads=cfg.B * cfg.H,
+                seconds=round(dt, 3), tflops=flop / dt / 1e12, cores=threads,
+                full_seconds_extrapolated=round(dt * work_full / work_sample, 1),
+                note="full-problem time extrapolated by the ratio of per-row work sum(i+1)")
 
 
 def main():
@@ -298,6 +403,18 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the shader clock under the forward alone: back-to-back fa_fwd calls
+    # while a host thread samples the clock (outside the timed steps)
+    log("sampling the shader clock under the forward")
+    with ClockSampler() as clk:
+        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ce0.record(stream)
+        for _ in range(40):
+            fa.fa_fwd(qd, kd, vd, o, lse, B, H, N, d, fscale, True, stream=stream)
+        ce1.record(stream)
+        torch.cuda.synchronize()
+    clock = clk.result()
+    clock_fwd_ms = ce0.elapsed_time(ce1) / 40
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
     gqa_ms = [e[2].elapsed_time(e[3]) for e in evs]
@@ -389,12 +506,18 @@ def main():
                         "+ paged decode 64 seqs x 32 heads x 128, fp16, block 16, "
                         "ctx U[512,4096], 20000-block pool",
             "fwd": {"B": B, "H": H, "N": N, "d": d, "causal": True, "flop": flops,
-                    "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(min(fwd_ms), 4),
-                    "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2)},
+                    "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_median": round(median(fwd_ms), 4),
+                    "kernel_ms_min": round(min(fwd_ms), 4),
+                    "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+                    "clock": clock, "clock_loop_ms_per_call": round(clock_fwd_ms, 4),
+                    "pct_bf16_peak_at_observed_clock":
+                        round(100.0 * flops / (clock_fwd_ms * 1e-3) / 1e12
+                              / (PEAK_BF16_TFLOPS * clock["ghz_median"] / PEAK_CLOCK_GHZ), 2)
+                        if clock else None},
             "decode": {"num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D,
                        "block_size": BS, "sum_ctx": int(ctx.sum()), "max_ctx": maxctx,
                        "algorithmic_bytes": dec_bytes, "ms_avg": round(dec_avg, 4),
-                       "ms_min": round(min(dec_ms), 4)},
+                       "ms_median": round(median(dec_ms), 4), "ms_min": round(min(dec_ms), 4)},
             "outputs_finite": finite,
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -411,7 +534,7 @@ def main():
                                 "algorithmic_per_launch": dec_bytes}},
         "fwd_gqa": {"metric": "attention forward TFLOP/s, 4 query heads per kv head",
                     "value": round(qcfg.flops() / (fgqa_avg * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                    "workload": qcfg.name, "kernel_ms_avg": round(fgqa_avg, 4),
+                    "workload": qcfg.name, "kernel_ms_avg": round(fgqa_avg, 4), "ms_median": round(median(fgqa_ms), 4),
                     "kernel_ms_min": round(min(fgqa_ms), 4),
                     "roofline": {"bound": "mfma",
                                  "achieved": round(qcfg.flops() / (fgqa_avg * 1e-3) / 1e12, 2),
@@ -422,7 +545,7 @@ def main():
         "bwd": {"metric": "attention backward TFLOP/s (dQ, dK, dV; 5 products of 2*N^2*d "
                           "per head, halved for causal)",
                 "value": round(bwd_tflops, 2), "unit": "TFLOP/s", "workload": fcfg.name,
-                "ms_avg": round(bwd_avg, 4), "ms_min": round(min(bwd_ms), 4),
+                "ms_avg": round(bwd_avg, 4), "ms_median": round(median(bwd_ms), 4), "ms_min": round(min(bwd_ms), 4),
                 "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2),
                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
@@ -432,7 +555,7 @@ def main():
                              "algorithmic_per_launch": bwd_flops}},
         "fwd_fp8": {"metric": "attention forward TFLOP/s on block-scaled E4M3 inputs",
                     "value": round(f8_tflops, 2), "unit": "TFLOP/s", "workload": fcfg.name + ", E4M3",
-                    "kernel_ms_avg": round(f8_avg, 4), "kernel_ms_min": round(min(f8_ms), 4),
+                    "kernel_ms_avg": round(f8_avg, 4), "ms_median": round(median(f8_ms), 4), "kernel_ms_min": round(min(f8_ms), 4),
                     "speedup_vs_bf16": round(fwd_avg / f8_avg, 3),
                     "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 2),
                                  "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
@@ -488,7 +611,7 @@ def main():
         "decode_gqa": {"metric": "paged decode HBM bandwidth, 4 query heads per kv head",
                        "value": round(gqa_gbs, 1), "unit": "GB/s",
                        "workload": gcfg.name, "sum_ctx": int(gctx.sum()),
-                       "ms_avg": round(gqa_avg, 4), "ms_min": round(min(gqa_ms), 4),
+                       "ms_avg": round(gqa_avg, 4), "ms_median": round(median(gqa_ms), 4), "ms_min": round(min(gqa_ms), 4),
                        "roofline": {"bound": "hbm", "achieved": round(gqa_gbs, 1),
                                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                     "frac": round(gqa_gbs / PEAK_HBM_GBS, 4),
@@ -498,6 +621,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(q, k, v, fscale, True)
+        log("timing the CPU oracle on the long-context workload's sampled rows")
+        result["cpu_baseline"]["long_context_sample"] = cpu_long_context_sample()
     print(json.dumps(result), flush=True)
 
 
