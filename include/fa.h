@@ -86,10 +86,13 @@ enum {
  *   scale   : finite and >= 0 (usually 1/sqrt(d)); else FA_ERR_INVALID_ARG.
  *   causal  : non-zero: row i sees keys j <= i only (top-left aligned square
  *             mask, youngju.dev section 11.3); zero: all N keys.
- *   dtype   : FA_F32, FA_BF16 or FA_F16.  Products are exact and accumulate
- *             in fp32; the softmax probabilities are rounded (round to
- *             nearest even) to `dtype` before the P.V product on the matrix
- *             cores (kept in fp32 for FA_F32).
+ *   dtype   : FA_F32, FA_BF16 or FA_F16.  For FA_BF16 and FA_F16 the
+ *             elementwise products are exact in fp32 and accumulate in fp32;
+ *             for FA_F32 each product is rounded to fp32 (the matrix cores'
+ *             fp32 instruction) before it accumulates in fp32.  The softmax
+ *             probabilities are rounded (round to nearest even) to `dtype`
+ *             before the P.V product on the matrix cores (kept in fp32 for
+ *             FA_F32).
  *   stream  : hipStream_t or NULL.
  * q/k/v may alias each other; o and lse must not overlap any input.
  */

@@ -72,6 +72,37 @@ def test_golden_layout_numbers():
         ve["inner_iterations"]
 
 
+@pytest.mark.parametrize("t0,i0", [(0, 0), (5, 9), (15, 127), (10, 64), (3, 71)])
+def test_golden_layout_addresses_pin_oracle(t0, i0):
+    # The page's cache layouts, placed element by element from the golden
+    # file's shapes and x: K(token t, element i) of kv head h in block b at
+    # k_cache[b, h, i // x, t, i % x], V(t, i) at v_cache[b, h, i, t].  A
+    # one-hot query on element i0 and a dominant K(t0, i0) (all other keys 0)
+    # make the softmax one-hot at t0, so the oracle's output must be the V row
+    # stored for token t0, each element naming its own (t, i).
+    g = golden()
+    assert g["k_cache_shape"] == "[num_blocks, num_kv_heads, head_size/x, block_size, x]"
+    assert g["v_cache_shape"] == "[num_blocks, num_kv_heads, head_size, block_size]"
+    x = g["fp16"]["x"]
+    D, BS = g["block_example"]["head_size"], g["block_example"]["block_size"]
+    NB, Hkv, blk, h = 3, 2, 1, 1
+    kc = torch.zeros((NB, Hkv, D // x, BS, x), dtype=torch.float16)
+    vc = torch.zeros((NB, Hkv, D, BS), dtype=torch.float16)
+    for t in range(BS):
+        for i in range(D):
+            vc[blk, h, i, t] = (t * D + i) / 4.0  # exact in fp16 (at most 11 significant bits)
+    kc[blk, h, i0 // x, t0, i0 % x] = 60.0
+    q = torch.zeros((1, Hkv, D), dtype=torch.float16)
+    q[0, h, i0] = 1.0
+    tables = torch.tensor([[blk]], dtype=torch.int32)
+    lens = torch.tensor([BS], dtype=torch.int32)
+    out, lse = oracle.paged_decode(q, kc, vc, tables, lens, 1.0)
+    want = (t0 * D + np.arange(D)) / 4.0
+    # the other 15 keys score 0 against 60: relative weight 15 e^-60
+    assert np.allclose(out[0, h], want, rtol=0, atol=1e-20 + 600 * 15 * math.exp(-60))
+    assert abs(lse[0, h] - (60.0 + math.log1p(15 * math.exp(-60)))) < 1e-12
+
+
 def test_generator_layout_matches_page():
     g = golden()
     cfg = small_cfg()
