@@ -52,6 +52,13 @@ def lib_path() -> str:
     return os.path.join(_HERE, "libfa.so")
 
 
+def load_debug_library(path):
+    """Bind another build of the C ABI (the LDS-poisoning debug build); returns
+    the handle without replacing the product library."""
+    import ctypes
+    return _bind(ctypes.CDLL(path))
+
+
 def load_library():
     """Load libfa.so once; raise if it is not built."""
     global _LIB

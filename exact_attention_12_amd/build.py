@@ -11,6 +11,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfa.so")
+# Debug build: every kernel fills its LDS with NaN bytes before first use
+# (FA_DEBUG_POISON), so a read of LDS the launch never wrote shows up as NaN
+# in the outputs.  Tests only; the product loads LIB.
+LIB_POISON = os.path.join(HERE, "libfa_poison.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip",
                                                     "fa_decode.hip", "fa_capi.cpp")]
 
@@ -28,17 +32,21 @@ HIPCC_FLAGS = [
 ]
 
 
-def _compile(hipcc, src, obj):
+def _compile(hipcc, src, obj, extra=()):
     """One translation unit to a position-independent object; returns (src, rc, messages)."""
-    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra)
     res = subprocess.run([hipcc] + flags + ["-c", src, "-o", obj], capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
     return src, res.returncode, msgs
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libfa.so (always recompiles; one process per source file) and return its path."""
+def build(verbose: bool = False, poison: bool = False) -> str:
+    """Compile libfa.so (always recompiles; one process per source file) and return its path.
+
+    poison=True builds the LDS-poisoning debug library libfa_poison.so instead."""
+    extra = ["-DFA_DEBUG_POISON"] if poison else []
+    target = LIB_POISON if poison else LIB
     import concurrent.futures
     import shutil
     import tempfile
@@ -47,16 +55,16 @@ def build(verbose: bool = False) -> str:
     try:
         objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in SOURCES]
         if verbose:
-            print(" ".join([hipcc] + HIPCC_FLAGS + ["-c"] + SOURCES), flush=True)
+            print(" ".join([hipcc] + HIPCC_FLAGS + extra + ["-c"] + SOURCES), flush=True)
         workers = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
         with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
-            results = list(ex.map(lambda so: _compile(hipcc, *so), zip(SOURCES, objs)))
+            results = list(ex.map(lambda so: _compile(hipcc, *so, extra=extra), zip(SOURCES, objs)))
         for src, rc, msgs in results:
             if rc != 0:
                 raise RuntimeError("hipcc failed on %s (%d):\n%s" % (src, rc, "\n".join(msgs)))
             if verbose and msgs:
                 print("\n".join(msgs), flush=True)
-        tmp = LIB + ".tmp%d" % os.getpid()
+        tmp = target + ".tmp%d" % os.getpid()
         res = subprocess.run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
                              capture_output=True, text=True)
         if res.returncode != 0:
@@ -72,9 +80,10 @@ def build(verbose: bool = False) -> str:
     if chk.returncode != 0:
         os.remove(tmp)
         raise RuntimeError("built library does not load:\n" + chk.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, poison=True))

@@ -277,6 +277,7 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
     static_assert(C::PV_STEPS * C::DB == NP, "S/dP and dV/dK take the same number of pairs");
     using S = DkdvSched<NBQ, NP>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
+    poison_lds(smem, sizeof(smem));
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -575,6 +576,7 @@ void fa_bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T 
     constexpr int NKB = C::NB;                 // 32-key blocks per K/V tile
     constexpr int STAGEB = 2 * C::TILEB;       // K + V
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
+    poison_lds(smem, sizeof(smem));
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;

@@ -168,6 +168,9 @@ void fa_decode_partition_kernel(const T *__restrict__ q, const T *__restrict__ k
     __shared__ __attribute__((aligned(16))) float logits[kDecPart];
     __shared__ float red[2][kDecWaves];
     __shared__ float part[kDecWaves][kDecD];
+    poison_lds(logits, sizeof(logits));
+    poison_lds(red, sizeof(red));
+    poison_lds(part, sizeof(part));
 
     // q elements this lane dots with, packed: head groups g = lane/16 + 4c.
     u32x4 qv[4];
@@ -313,6 +316,10 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
     __shared__ __attribute__((aligned(16))) float logits[GM][kDecPart];
     __shared__ float red[2][GM][kDecWaves];
     __shared__ float part[kDecWaves][GM][kDecD];
+    poison_lds(qs, sizeof(qs));
+    poison_lds(logits, sizeof(logits));
+    poison_lds(red, sizeof(red));
+    poison_lds(part, sizeof(part));
 
     // Load order: the queries first, then every K block, then every V block,
     // so that the queries can be staged and the logits started while V is

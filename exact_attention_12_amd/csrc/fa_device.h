@@ -148,4 +148,22 @@ __device__ __forceinline__ float halves_sum(float x)
     return lo + hi;
 }
 
+// Debug builds (compiled with FA_DEBUG_POISON): fill an LDS array with 0xff
+// bytes -- NaN as fp32, bf16 and fp16 -- and wait for the whole workgroup,
+// before the kernel's first LDS write.  A later read of a slot that this
+// launch never wrote then yields NaN instead of whatever an earlier
+// workgroup left there.  Every thread of the workgroup must call it (no
+// thread may have returned).  A no-op in the product build.
+__device__ __forceinline__ void poison_lds(void *p, int bytes)
+{
+#ifdef FA_DEBUG_POISON
+    const int nthreads = (int)(blockDim.x * blockDim.y * blockDim.z);
+    for (int i = (int)threadIdx.x; i < bytes / 4; i += nthreads) ((uint32_t *)p)[i] = 0xffffffffu;
+    __syncthreads();
+#else
+    (void)p;
+    (void)bytes;
+#endif
+}
+
 }  // namespace fa

@@ -98,6 +98,8 @@ __global__ __launch_bounds__(256) void fa_quant_fp8_kernel(const T *__restrict__
     constexpr int CPR = DD / VEC;                 // loads per row
     __shared__ float red[4];
     __shared__ __attribute__((aligned(16))) uint8_t tile[f8::QBLK * DD];
+    poison_lds(red, sizeof(red));
+    poison_lds(tile, sizeof(tile));
 
     const int nblk = (N + f8::QBLK - 1) / f8::QBLK;
     const int64_t bh = blockIdx.x / nblk;
@@ -208,6 +210,7 @@ void fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict_
 {
     using namespace f8;
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
+    poison_lds(smem, sizeof(smem));
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;

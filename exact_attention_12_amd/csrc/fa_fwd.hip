@@ -123,6 +123,7 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     constexpr int SB = C::STAGEB + MASKB;                        // bytes per stage
     auto swzm = [](int row) { return MCPR == 4 ? (row >> 2) & 3 : (row >> 3) & 1; };
     __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
+    poison_lds(smem, sizeof(smem));
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -877,6 +878,8 @@ void fa_mask_blocks_kernel(const uint8_t *__restrict__ mask, int Hs, int Nq, int
         if (((L >> (4 * i)) & 0xfu) == 0xfu) bl |= 1u << i;
     }
     __shared__ uint32_t sa[4], sl[4];
+    poison_lds(sa, sizeof(sa));
+    poison_lds(sl, sizeof(sl));
     if (lane == 0) {
         sa[wave] = ba;
         sl[wave] = bl;
