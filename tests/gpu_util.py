@@ -18,8 +18,17 @@ DECODE_TOL = dict(o_max=1e-2, o_mean=1e-3)
 # Backward (16-bit inputs, fp32 outputs): per gradient tensor, the largest
 # error against the largest reference magnitude, and the mean error against
 # the mean reference magnitude, each with a small absolute floor for
-# gradients that are exactly zero in the reference (N = 1).
-BWD_TOL = dict(max_rel=2e-2, mean_rel=5e-3, floor=1e-5)
+# gradients that are exactly zero in the reference (N = 1).  The kernel
+# rounds two fp32 intermediates to the input type before a matrix product
+# -- P (recomputed from lse) for dV = P^T dO and dS = P o (dP - D) for
+# dQ = dS K and dK = dS^T Q -- and accumulates the exact 16-bit products in
+# fp32, so the error is a sum of terms each carrying one relative rounding
+# of at most u (2^-8 for bf16, 2^-11 for fp16).  Measured over the shapes of
+# test_gpu_bwd.py (ragged, d 64/128, grouped kv heads, full-size rows): the
+# largest max ratio is 0.78 u and the largest mean ratio 0.45 u, for both
+# types.  The bars are 2 u and 1.25 u, about 2.7 times those.
+_U = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+BWD_TOL = {dt: dict(max_rel=2.0 * u, mean_rel=1.25 * u, floor=1e-5) for dt, u in _U.items()}
 # Block-scaled FP8 forward, against the oracle on the dequantised inputs.
 # The only rounding beyond fp32 accumulation is that of each probability to
 # E4M3 before the P.V product: |P^ - P~| <= 2^-4 P~ in the normal range and
@@ -81,9 +90,10 @@ def assert_bwd_close(dq, dk, dv, ref, dtype, label=""):
         out[name] = (emax, emean, rmax, rmean)
         progress("%s %s max|err|=%.3g mean|err|=%.3g max|ref|=%.3g mean|ref|=%.3g" % (
             label, name, emax, emean, rmax, rmean))
+    tol = BWD_TOL[dtype]
     for name, (emax, emean, rmax, rmean) in out.items():
-        assert emax <= BWD_TOL["max_rel"] * rmax + BWD_TOL["floor"], (label, name, emax, rmax)
-        assert emean <= BWD_TOL["mean_rel"] * rmean + BWD_TOL["floor"], (label, name, emean, rmean)
+        assert emax <= tol["max_rel"] * rmax + tol["floor"], (label, name, emax, rmax)
+        assert emean <= tol["mean_rel"] * rmean + tol["floor"], (label, name, emean, rmean)
     return out
 
 
