@@ -199,6 +199,102 @@ __global__ __launch_bounds__(256) void fa_quant_fp8_kernel(const T *__restrict__
 
 // ---------------------------------------------------------------------------
 // FP8 forward
+// Quantisation to the d-major V layout without an LDS pass: thread (g, j)
+// of a workgroup takes rows RT g .. RT g + RT-1 and columns 8 j .. 8 j + 7 of
+// the 128-row block (RT = 8 for d = 128, 4 for d = 64), computes their codes
+// as above, transposes its RT x 8 bytes in registers, and writes for each of
+// its 8 columns the RT consecutive keys that the output holds contiguously:
+// byte (t, col, key) = code (64 t + key, col).  Rows past N are written as
+// code 0 up to the end of their 64-key tile.
+template <typename T, int DD>
+__global__ __launch_bounds__(256) void fa_quant_fp8_vt_kernel(const T *__restrict__ X,
+                                                              uint8_t *__restrict__ codes,
+                                                              int32_t *__restrict__ exps, int N)
+{
+    constexpr int RT = f8::QBLK * DD / 256 / 8;  // rows per thread (8 columns each)
+    constexpr int NGR = f8::QBLK / RT;           // row groups
+    static_assert(NGR * (DD / 8) == 256, "one 8-column x RT-row piece per thread");
+    constexpr int ES = (int)sizeof(T);
+    constexpr int LPR = 8 * ES / 16;             // 16-byte loads per 8 columns of a row
+    constexpr int VEC = 16 / ES;
+    __shared__ float red[4];
+    poison_lds(red, sizeof(red));
+
+    const int nblk = (N + f8::QBLK - 1) / f8::QBLK;
+    const int64_t bh = blockIdx.x / nblk;
+    const int blk = blockIdx.x % nblk;
+    const int r0 = blk * f8::QBLK;
+    const int rows = min(f8::QBLK, N - r0);
+    const int tid = threadIdx.x;
+    const int g = tid % NGR, j = tid / NGR;
+    const T *src = X + (bh * N + r0) * DD + 8 * j;
+
+    typedef T tvec __attribute__((ext_vector_type(VEC)));
+    float v[RT][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const int row = RT * g + i;
+#pragma unroll
+        for (int l = 0; l < LPR; ++l) {
+            if (row < rows) {
+                const tvec x = __builtin_nontemporal_load((const tvec *)(src + (int64_t)row * DD + l * VEC));
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    v[i][l * VEC + e] = (float)x[e];
+                    amax = fmaxf(amax, fabsf(v[i][l * VEC + e]));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) v[i][l * VEC + e] = 0.f;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m /= 2) amax = fmaxf(amax, __shfl_xor(amax, m));
+    if (tid % kWave == 0) red[tid / kWave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    if (amax > 0.f) {
+        int ex;
+        frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1)
+        e = (ex - 1) - 7;
+    }
+    if (tid == 0) exps[bh * nblk + blk] = e;
+
+    // codes of row i: w[i][0] = columns 0..3, w[i][1] = columns 4..7 (byte c % 4)
+    uint32_t w[RT][2];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+            const float *x = &v[i][4 * hlf];
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[0], -e), ldexpf(x[1], -e), 0, false);
+            w[i][hlf] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[2], -e), ldexpf(x[3], -e), lo, true);
+        }
+    const int ntile = (N + 63) / 64;
+    const int t = 2 * blk + (RT * g) / 64, key0 = (RT * g) % 64;
+    if (t >= ntile) return;
+    uint8_t *dst = codes + ((bh * ntile + t) * DD + 8 * j) * 64 + key0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        // keys key0 .. key0 + RT-1 of column 8 j + c, 4 per word
+        uint32_t o[RT / 4];
+#pragma unroll
+        for (int q = 0; q < RT / 4; ++q) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) word |= ((w[4 * q + b][c / 4] >> (8 * (c % 4))) & 0xffu) << (8 * b);
+            o[q] = word;
+        }
+        if constexpr (RT == 8)
+            *(u32x2 *)(dst + c * 64) = u32x2{o[0], o[1]};
+        else
+            *(uint32_t *)(dst + c * 64) = o[0];
+    }
+}
+
 // ---------------------------------------------------------------------------
 template <bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
@@ -485,7 +581,7 @@ static hipError_t launch_quant(const void *x, int B, int H, int N, int layout, v
         hipLaunchKernelGGL((fa_quant_fp8_kernel<T, DD, 0>), grid, dim3(256), 0, stream, (const T *)x,
                            (uint8_t *)codes, exps, N);
     else
-        hipLaunchKernelGGL((fa_quant_fp8_kernel<T, DD, 1>), grid, dim3(256), 0, stream, (const T *)x,
+        hipLaunchKernelGGL((fa_quant_fp8_vt_kernel<T, DD>), grid, dim3(256), 0, stream, (const T *)x,
                            (uint8_t *)codes, exps, N);
     return hipGetLastError();
 }
