@@ -480,9 +480,9 @@ def main():
                  + int(((gctx + BS - 1) // BS).sum()) * 4 + S * 4)
     gqa_gbs = gqa_bytes / (gqa_avg * 1e-3) / 1e9
 
-    fwd_hash = source_hash("fa_fwd.hip", "fa_device.h", "fa_tile.h")
-    bwd_hash = source_hash("fa_bwd.hip", "fa_device.h", "fa_tile.h")
-    dec_hash = source_hash("fa_decode.hip", "fa_device.h", "fa_tile.h")
+    fwd_hash = source_hash("fa_fwd.hip", "fa_device.h", "fa_tile.h", "fa_sizes.h")
+    bwd_hash = source_hash("fa_bwd.hip", "fa_device.h", "fa_tile.h", "fa_sizes.h")
+    dec_hash = source_hash("fa_decode.hip", "fa_device.h", "fa_tile.h", "fa_sizes.h")
     fwd_traffic = measured_traffic("fa_fwd_kernel", fwd_hash)
     dec_traffic = measured_traffic("fa_decode_partition_kernel", dec_hash)
     bwd_traffic = measured_traffic("fa_bwd", bwd_hash)
@@ -568,7 +568,7 @@ def main():
                       "roofline": {"bound": "hbm", "achieved": round(qz_gbs, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": round(qz_gbs / PEAK_HBM_GBS, 4),
-                                   "kernel": "fa_quant_fp8_kernel x3",
+                                   "kernel": "fa_quant_fp8_kernel (q, k) + fa_quant_fp8_vt_kernel (v)",
                                    "algorithmic_per_launch": qz_bytes}},
         "fwd_window": {"metric": "attention forward TFLOP/s over visible pairs, causal sliding window",
                        "value": round(win_tf, 2), "unit": "TFLOP/s",
