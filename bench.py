@@ -93,11 +93,11 @@ def cpu_model():
     return None
 
 
-def _sclk_sources():
-    """sysfs files that report the GPU's current shader clock: pp_dpm_sclk, whose
-    starred line is the current frequency."""
+def _clk_sources(kind="sclk"):
+    """sysfs files that report a current GPU clock: pp_dpm_sclk (shader) or
+    pp_dpm_mclk (memory), whose starred line is the current frequency."""
     import glob
-    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_%s" % kind))
 
 
 def _read_sclk_ghz(path):
@@ -110,14 +110,15 @@ def _read_sclk_ghz(path):
 
 
 class ClockSampler:
-    """Samples the GPU shader clock from sysfs every few milliseconds on a host
-    thread while the GPU runs; reports the median in GHz (None if unreadable).
-    With several cards visible, the one whose clock moves most is taken."""
+    """Samples a GPU clock (kind "sclk" or "mclk") from sysfs every few
+    milliseconds on a host thread while the GPU runs; reports the median in GHz
+    (None if unreadable).  With several cards visible, the one whose clock
+    moves most is taken."""
 
-    def __init__(self, period_s=0.002):
+    def __init__(self, period_s=0.002, kind="sclk"):
         import threading
         self.period = period_s
-        self.files = _sclk_sources()
+        self.files = _clk_sources(kind)
         self.samples = {f: [] for f in self.files}
         self._stop = threading.Event()
         self._t = threading.Thread(target=self._run, daemon=True)
@@ -405,8 +406,8 @@ def main():
     wall = time.perf_counter() - t0
     # the shader clock under the forward alone: back-to-back fa_fwd calls
     # while a host thread samples the clock (outside the timed steps)
-    log("sampling the shader clock under the forward")
-    with ClockSampler() as clk:
+    log("sampling the shader and memory clocks under the forward")
+    with ClockSampler() as clk, ClockSampler(kind="mclk") as mclk:
         ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ce0.record(stream)
         for _ in range(40):
@@ -414,6 +415,7 @@ def main():
         ce1.record(stream)
         torch.cuda.synchronize()
     clock = clk.result()
+    mem_clock = mclk.result()
     clock_fwd_ms = ce0.elapsed_time(ce1) / 40
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
@@ -509,7 +511,7 @@ def main():
                     "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_median": round(median(fwd_ms), 4),
                     "kernel_ms_min": round(min(fwd_ms), 4),
                     "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-                    "clock": clock, "clock_loop_ms_per_call": round(clock_fwd_ms, 4),
+                    "clock": clock, "memory_clock": mem_clock, "clock_loop_ms_per_call": round(clock_fwd_ms, 4),
                     "pct_bf16_peak_at_observed_clock":
                         round(100.0 * flops / (clock_fwd_ms * 1e-3) / 1e12
                               / (PEAK_BF16_TFLOPS * clock["ghz_median"] / PEAK_CLOCK_GHZ), 2)

@@ -13,7 +13,9 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfa.so")
 # Debug build: every kernel fills its LDS with NaN bytes before first use
 # (FA_DEBUG_POISON), so a read of LDS the launch never wrote shows up as NaN
-# in the outputs.  Tests only; the product loads LIB.
+# in the outputs, and every entry point waits for its stream before it
+# returns (FA_DEBUG_SYNC), so a device fault is reported by the call that
+# caused it.  Tests only; the product loads LIB.
 LIB_POISON = os.path.join(HERE, "libfa_poison.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip",
                                                     "fa_decode.hip", "fa_capi.cpp")]
@@ -44,8 +46,9 @@ def _compile(hipcc, src, obj, extra=()):
 def build(verbose: bool = False, poison: bool = False) -> str:
     """Compile libfa.so (always recompiles; one process per source file) and return its path.
 
-    poison=True builds the LDS-poisoning debug library libfa_poison.so instead."""
-    extra = ["-DFA_DEBUG_POISON"] if poison else []
+    poison=True builds the debug library libfa_poison.so instead (LDS poisoning, and a
+    stream synchronisation at the end of every call)."""
+    extra = ["-DFA_DEBUG_POISON", "-DFA_DEBUG_SYNC"] if poison else []
     target = LIB_POISON if poison else LIB
     import concurrent.futures
     import shutil

@@ -69,6 +69,22 @@ bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb)
 
 bool valid_scale(float s) { return std::isfinite(s) && s >= 0.f; }
 
+// Status of a call whose work was enqueued with result e.  A library built
+// with FA_DEBUG_SYNC (the debug build) also waits for the stream, so that a
+// fault of the launched kernels is reported, as FA_ERR_HIP, by the call that
+// launched them instead of by a later call; such a build cannot be used
+// under stream capture.
+int launched(hipError_t e, void *stream)
+{
+#ifdef FA_DEBUG_SYNC
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess) e = hipGetLastError();
+#else
+    (void)stream;
+#endif
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 namespace {
@@ -102,7 +118,7 @@ int fwd_checked(const void *q, const void *k, const void *v, float *o, float *ls
             return FA_ERR_INVALID_ARG;
     const hipError_t e = fa::fwd_dispatch(q, k, v, o, lse, B, H, Hkv, N, d, scale,
                                           causal ? 1 : 0, dtype, (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 }  // namespace
@@ -160,7 +176,7 @@ extern "C" int fa_mask_blocks(const uint8_t *mask, int B, int H, int Nq, int Nk,
         return FA_ERR_INVALID_ARG;
     const hipError_t e = fa::mask_blocks_dispatch(mask, B, H, Nq, Nk, mask_stride_b, mask_stride_h,
                                                   (int)mask_ld, blocks, (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 extern "C" int fa_fwd_ext(const void *q, const void *k, const void *v, float *o, float *lse, int B,
@@ -203,7 +219,7 @@ extern "C" int fa_fwd_ext(const void *q, const void *k, const void *v, float *o,
         fa::fwd_ext_dispatch(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, window_left,
                              window_right, mask, mask_stride_b, mask_stride_h, (int)mask_ld,
                              mask_blocks, dtype, (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 extern "C" int fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
@@ -244,7 +260,7 @@ extern "C" int fa_fwd_paged(const void *q, const void *k_cache, const void *v_ca
                                                 num_seqs, num_heads, num_kv_heads, Nq, max_blocks_per_seq,
                                                 cache_bytes, scale, causal ? 1 : 0, dtype,
                                                 (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 extern "C" size_t fa_bwd_workspace_size(int B, int H, int N)
@@ -290,7 +306,7 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const float *
     }
     const hipError_t e = fa::bwd_dispatch(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale,
                                           causal ? 1 : 0, dtype, workspace, (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 extern "C" size_t fa_fp8_codes_bytes(int B, int H, int N, int d, int layout)
@@ -320,7 +336,7 @@ extern "C" int fa_quant_fp8(const void *x, int dtype, int B, int H, int N, int d
         return FA_ERR_INVALID_ARG;
     const hipError_t e = fa::quant_fp8_dispatch(x, dtype, B, H, N, d, layout, codes, exps,
                                                 (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 extern "C" int fa_fwd_fp8(const void *q8, const void *k8, const void *v8, const int32_t *q_exp,
@@ -351,7 +367,7 @@ extern "C" int fa_fwd_fp8(const void *q8, const void *k8, const void *v8, const 
             return FA_ERR_INVALID_ARG;
     const hipError_t e = fa::fwd_fp8_dispatch(q8, k8, v8, q_exp, k_exp, v_exp, o, lse, B, H, Hkv, N,
                                               scale, causal ? 1 : 0, (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 extern "C" size_t fa_paged_decode_workspace_size(int num_seqs, int num_heads, int head_size,
@@ -426,7 +442,7 @@ extern "C" int fa_paged_decode(const void *q, const void *k_cache, const void *v
                                              num_seqs, num_heads, num_kv_heads, max_blocks_per_seq,
                                              max_context_len, scale, dtype, workspace,
                                              (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 extern "C" int fa_paged_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
@@ -453,7 +469,7 @@ extern "C" int fa_paged_decode_noalloc(const void *q, const void *k_cache, const
                                                      out, num_seqs, num_heads, num_kv_heads,
                                                      max_blocks_per_seq, max_context_len, scale,
                                                      dtype, (hipStream_t)stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return launched(e, stream);
 }
 
 extern "C" const char *fa_strerror(int status)

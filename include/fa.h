@@ -37,7 +37,10 @@
  *  - Arguments are validated on the host before anything is launched.  On a
  *    non-zero status nothing was launched and nothing was written.  A launch
  *    failure reported by the HIP runtime returns FA_ERR_HIP.  Device faults
- *    surface at the caller's next synchronisation.
+ *    surface at the caller's next synchronisation.  (The debug build of the
+ *    library, compiled with FA_DEBUG_SYNC, waits for `stream` before every
+ *    call returns and reports a fault of the call's own kernels as
+ *    FA_ERR_HIP; it cannot be used under stream capture.)
  *  - Thread-safe.  Deterministic: identical inputs give bitwise identical
  *    outputs (fixed reduction order, no atomics).
  */

@@ -36,6 +36,19 @@ def test_exports_every_declared_function(fa_lib):
         assert hasattr(fa_lib, n), n
 
 
+def test_product_library_never_synchronises(fa_lib):
+    # every call only enqueues work (so that it can be captured into a graph):
+    # the product library must not import a synchronising or allocating HIP call
+    import subprocess
+    import exact_attention_12_amd as fa
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    imported = {ln.split()[-1].split("@")[0] for ln in out.splitlines() if ln.strip()}
+    for name in ("hipStreamSynchronize", "hipDeviceSynchronize", "hipMalloc", "hipFree", "hipMemset",
+                 "hipMemsetAsync", "hipMallocAsync", "hipExtMallocWithFlags"):
+        assert name not in imported, name
+
+
 def test_strerror(fa_lib):
     for st, word in [(OK, "success"), (INVALID, "invalid"), (UNSUPPORTED, "unsupported"),
                      (ALIGN, "align"), (WORKSPACE, "workspace"), (HIP, "HIP"), (SCRATCH, "scratch")]:
