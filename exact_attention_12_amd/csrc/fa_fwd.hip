@@ -7,13 +7,14 @@
 // Attention", suniverse77.github.io, Eq. (1)-(4)).
 //
 // Work decomposition (FlashAttention-2 order, youngju.dev sections 8.2-8.3):
-//  - one workgroup of 4 waves per (b, h, 128-row query tile); the query tile
-//    is split across the waves, 32 rows each, with no communication between
-//    waves (split-Q).  Causal: a workgroup takes a heavy and a light query
-//    tile of the same head one after the other, so all workgroups carry
-//    about the same work;
+//  - one workgroup of NW waves per (b, h, 32 NW-row query tile): 8 waves
+//    (256 rows) for the plain forward on 16-bit inputs at d = 128, 4 waves
+//    (128 rows) otherwise; the query tile is split across the waves, 32 rows each,
+//    with no communication between waves (split-Q).  Causal: a workgroup
+//    takes a heavy and a light query tile of the same head one after the
+//    other, so all workgroups carry about the same work;
 //  - every wave keeps its Q rows in registers as matrix-core operands; the
-//    K/V tiles (BC keys each) that all four waves share stream from HBM
+//    K/V tiles (BC keys each) that all the waves share stream from HBM
 //    straight into LDS (16-byte direct-to-LDS loads, no register staging),
 //    double buffered, row-major with an XOR swizzle of the 16-byte chunks
 //    that keeps both read patterns below free of bank conflicts;
@@ -43,12 +44,12 @@
 
 namespace fa {
 
-template <typename T, int D> struct FwdCfg {
+template <typename T, int D, int NW = 4> struct FwdCfg {
     static constexpr int KW = Mma<T>::KW;
     static constexpr int ES = (int)sizeof(T);
     static constexpr int VEC = 16 / ES;              // elements per 16-byte chunk
-    static constexpr int NT = 256;                    // threads per workgroup (4 waves)
-    static constexpr int BR = 128;                    // query rows per workgroup
+    static constexpr int NT = NW * kWave;             // threads per workgroup (NW waves)
+    static constexpr int BR = NW * 32;                // query rows per workgroup
     static constexpr int BC = (ES == 4) ? 32 : 64;    // keys per K/V tile
     static constexpr int NKB = BC / 32;               // 32-key blocks per tile
     static constexpr int CPR = D / VEC;               // 16-byte chunks per row
@@ -56,13 +57,14 @@ template <typename T, int D> struct FwdCfg {
     static constexpr int TILEB = BC * ROWB;           // bytes per K or V tile
     static constexpr int STAGEB = 2 * TILEB;          // K + V
     static constexpr int NLD = BC * CPR / kWave;      // direct-to-LDS loads per tile
-    static constexpr int NLD_W = NLD / 4;             // ... per wave
+    static constexpr int NLD_W = NLD / NW;            // ... per wave
     static constexpr int QK_STEPS = D / (2 * KW);     // MFMA steps over d for S
     static constexpr int PV_STEPS = 32 / (2 * KW);    // MFMA steps per 32-key block for PV
     static constexpr int DB = D / 32;                 // 32-row blocks of O^T
-    // waves per SIMD: two (two workgroups per CU) when the registers allow
+    // waves per SIMD: two when the registers allow
     static constexpr int WPE = (ES == 4 && D == 128) ? 1 : 2;
-    static_assert(NLD % 4 == 0, "tile loads must split evenly over the waves");
+    static_assert(NLD % NW == 0, "tile loads must split evenly over the waves");
+    static_assert(NW == 4 || NW == 8, "workgroups of 4 or 8 waves");
     static_assert(D % 32 == 0 && BC % 32 == 0, "tile shapes");
 };
 
@@ -99,19 +101,34 @@ struct FwdExt {
 // plus a boolean mask, 3 = 2 with the mask's block map, 4 = 1 with K/V read
 // from the paged cache (the number of keys and the diagonal's offset come
 // from each sequence's context length).
+// Waves per workgroup.  The plain forward on 16-bit inputs at d = 128 takes
+// 8: 256 query rows share each K/V tile, so every tile is loaded into LDS
+// once per 256 rows instead of per 128, with one workgroup (two waves per
+// SIMD) per CU; measured 1.4-4 % faster than two 4-wave workgroups per CU.
+// At d = 64 (155 registers) three 4-wave workgroups fit a CU, and 8 waves
+// measured ~10 % slower.  fp32 (one wave per SIMD at d = 128) and the
+// general-mask and paged forms, whose block maps and cache walks are laid
+// out for 128-row workgroups, take 4.
+template <typename T, int D, int EXT> constexpr int fwd_waves()
+{
+    return (EXT == 0 && sizeof(T) == 2 && D == 128) ? 8 : 4;
+}
+
 template <typename T, int D, bool CAUSAL, int EXT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+__global__ __attribute__((amdgpu_flat_work_group_size(FwdCfg<T, D, fwd_waves<T, D, EXT>()>::NT,
+                                                      FwdCfg<T, D, fwd_waves<T, D, EXT>()>::NT),
                           amdgpu_waves_per_eu(FwdCfg<T, D>::WPE, FwdCfg<T, D>::WPE)))
 void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                    float *__restrict__ O, float *__restrict__ LSE, int N, int num_qtiles,
                    float scale, int H, int group, FwdExt ext)
 {
     static_assert(EXT == 0 || !CAUSAL, "general masks fold causality into the window");
-    using C = FwdCfg<T, D>;
+    using C = FwdCfg<T, D, fwd_waves<T, D, EXT>()>;
     constexpr bool HAS_MASK = EXT == 2 || EXT == 3;  // a boolean mask rides along
     static_assert(EXT != 4 || (C::ES == 2 && D == 128 && C::BC == 64 && C::NLD_W == 4),
                   "paged K/V: each wave loads one 16-token cache block of K and of V per tile");
-    static_assert(C::BR == 128 && 64 % C::BC == 0, "a block of the mask's map (128 x 64) is whole tiles");
+    static_assert(EXT != 3 || (C::BR == 128 && 64 % C::BC == 0),
+                  "a block of the mask's map (128 x 64) is whole tiles");
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int KW = C::KW;
@@ -760,7 +777,7 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
                              int B, int H, int Hkv, int N, float scale, hipStream_t stream)
 {
-    using C = FwdCfg<T, D>;
+    using C = FwdCfg<T, D, fwd_waves<T, D, 0>()>;
     const int nqt = (N + C::BR - 1) / C::BR;
     const int64_t grid = (int64_t)B * H * (CAUSAL ? (nqt + 1) / 2 : nqt);
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 0>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
@@ -774,7 +791,7 @@ static hipError_t launch_fwd_ext(const void *q, const void *k, const void *v, fl
                                  int B, int H, int Hkv, int Nq, float scale, const FwdExt &ext,
                                  hipStream_t stream)
 {
-    using C = FwdCfg<T, D>;
+    using C = FwdCfg<T, D, 4>;  // EXT 1..3: fwd_waves() is 4
     const int nqt = (Nq + C::BR - 1) / C::BR;
     const int64_t grid = (int64_t)B * H * nqt;
     if (ext.mask && ext.blocks)
