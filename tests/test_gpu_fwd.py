@@ -101,6 +101,20 @@ def test_ragged_shapes(gpu, fa_lib, dt, d, causal, N):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [600, 1100, 1290])
+def test_query_tile_counts(gpu, fa_lib, dt, causal, N):
+    # d = 128 on 16-bit inputs runs 256-row workgroups: 3, 5 and 6 query
+    # tiles (for odd counts the causal pairing leaves the middle tile to run
+    # alone) with ragged last tiles of 88, 76 and 10 rows; at 128 rows
+    # (d = 64) the same N give 5, 9 and 11 tiles
+    for d in (128, 64):
+        cfg = inputs.FwdConfig(cid=61 + N % 13, B=1, H=3, N=N, d=d, dtype=DT[dt], causal=causal,
+                               qk_factor=1.5, name="tiles %s d%d N%d causal%d" % (dt, d, N, causal))
+        check_cfg(cfg, gpu)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_long_ragged_causal(gpu, fa_lib, dt):
     cfg = inputs.FwdConfig(cid=70, B=1, H=4, N=1000, d=128, dtype=DT[dt], causal=True,
                            qk_factor=2.0, name="long ragged %s" % dt)
