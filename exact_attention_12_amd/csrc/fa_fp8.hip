@@ -65,6 +65,9 @@ constexpr int QSTEPS = D / 64;    // matrix steps over d
 constexpr int DB = D / 32;        // 32-row blocks of O^T
 constexpr int QBLK = 128;         // rows per quantisation block
 constexpr float kPMax = 256.0f;   // bound on P~: every value is a finite E4M3 number
+// the forward takes one Q block exponent per workgroup: its query tile must be
+// exactly one quantisation block
+static_assert(BR == QBLK, "a query tile is one block of Q's scales");
 
 // 16-byte chunk swizzles (position = chunk ^ swz(row)); both keep a 16-lane
 // pass of row-fragment reads (16 consecutive rows, one chunk) on 16 distinct
