@@ -16,8 +16,11 @@
 //  - every wave keeps its Q rows in registers as matrix-core operands; the
 //    K/V tiles (BC keys each) that all the waves share stream from HBM
 //    straight into LDS (16-byte direct-to-LDS loads, no register staging),
-//    double buffered, row-major with an XOR swizzle of the 16-byte chunks
-//    that keeps both read patterns below free of bank conflicts;
+//    row-major with an XOR swizzle of the 16-byte chunks that keeps both
+//    read patterns below free of bank conflicts.  Double buffered with one
+//    barrier per tile, or, for the 8-wave form, a 4-slot ring whose tiles
+//    go in pairs: a pair loads the next two tiles, computes its two, and
+//    takes one barrier;
 //  - S^T = K Q^T is formed on the matrix cores, so each lane owns one query
 //    row and 16 keys of each 32-key block: the row max and the row sum are
 //    in-lane except for one exchange between the two lane halves;
@@ -44,7 +47,8 @@
 
 namespace fa {
 
-template <typename T, int D, int NW = 4> struct FwdCfg {
+template <typename T, int D, int NWV = 4> struct FwdCfg {
+    static constexpr int NW = NWV;                    // waves per workgroup
     static constexpr int KW = Mma<T>::KW;
     static constexpr int ES = (int)sizeof(T);
     static constexpr int VEC = 16 / ES;              // elements per 16-byte chunk
@@ -101,6 +105,19 @@ struct FwdExt {
 // plus a boolean mask, 3 = 2 with the mask's block map, 4 = 1 with K/V read
 // from the paged cache (the number of keys and the diagonal's offset come
 // from each sequence's context length).
+// Transpose read (ds_read_b64_tr_b16) through a restrict parameter: once
+// inlined, the read carries alias-scope information, and the compiler's
+// wait-count insertion then does not wait for direct-to-LDS loads still in
+// flight before it (without it, every pair of tiles of the 4-slot ring waits
+// for both next tiles' loads in the middle of its first tile).  Valid where
+// the loads in flight never target the slot being read: in the 4-slot ring
+// a pair reads slots whose loads were waited for (vmcnt(0), then a barrier)
+// at the end of the previous pair, while it loads the other two.
+__device__ __forceinline__ s16x4 lds_read_tr16_scoped(const lds_s16x4 *__restrict__ p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+}
+
 // Waves per workgroup.  The plain forward on 16-bit inputs at d = 128 takes
 // 8: 256 query rows share each K/V tile, so every tile is loaded into LDS
 // once per 256 rows instead of per 128, with one workgroup (two waves per
@@ -139,7 +156,10 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     constexpr int NLDM_W = HAS_MASK ? C::BR * MCPR / kWave / 4 : 0;  // its 1 KiB loads per wave
     constexpr int SB = C::STAGEB + MASKB;                        // bytes per stage
     auto swzm = [](int row) { return MCPR == 4 ? (row >> 2) & 3 : (row >> 3) & 1; };
-    __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
+    // LDS ring of K/V tiles: 2 slots (one barrier per tile), or 4 for the
+    // 8-wave plain forward, whose tiles go in pairs (one barrier per two tiles)
+    constexpr int RING = (EXT == 0 && C::NW == 8) ? 4 : 2;
+    __shared__ __attribute__((aligned(1024))) char smem[RING * SB];
     poison_lds(smem, sizeof(smem));
 
     const int tid = threadIdx.x;
@@ -476,13 +496,17 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         return (part[0] + part[1]) + (part[2] + part[3]);
     };
 
-    // One K/V tile: j is the tile, STAGE its LDS buffer; jn is the tile to
+    // One K/V tile: j is the tile, STAGE its LDS slot; jn is the tile to
     // load next (ntiles: none).  Boolean mask: part (part_n) tells whether
     // tile j (jn) needs its mask bytes; without them it is fully visible.
-    auto tile = [&](int j, int jn, bool part, bool part_n, auto stage_c) {
+    // SYNC: the tile issues the load of jn into the other of two slots and
+    // ends with the barrier; otherwise it only computes (the 4-slot ring's
+    // pairs load and synchronise around two tiles).
+    auto tile = [&](int j, int jn, bool part, bool part_n, auto stage_c, auto sync_c) {
         constexpr int STAGE = decltype(stage_c)::value;
+        constexpr bool SYNC = decltype(sync_c)::value;
         const int k0 = j * C::BC;
-        if (jn < ntiles) load_tile(jn, STAGE ^ 1, part_n);
+        if (SYNC && jn < ntiles) load_tile(jn, STAGE ^ 1, part_n);
         uint32_t mcur[C::NKB][4];
         if constexpr (HAS_MASK) {
             if (part) {
@@ -513,8 +537,10 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             }
         }
         if (skip) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+            if constexpr (SYNC) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+            }
             return;
         }
         f32x16 s[C::NKB];
@@ -600,10 +626,14 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                         // 4*(g/2) + r/4 (+8), elements db*32 + 16*(g%2) +
                         // 4*(r%4) .. +3.
                         const char *vblk = Vs + (kb * 32 + 16 * st) * C::ROWB;
-                        const s16x4 lo =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[0][db]));
-                        const s16x4 hi =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[1][db]));
+                        s16x4 lo, hi;
+                        if constexpr (RING == 4) {
+                            lo = lds_read_tr16_scoped((const lds_s16x4 *)(vblk + v_rd[0][db]));
+                            hi = lds_read_tr16_scoped((const lds_s16x4 *)(vblk + v_rd[1][db]));
+                        } else {
+                            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[0][db]));
+                            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vblk + v_rd[1][db]));
+                        }
                         a = __builtin_bit_cast(frag,
                                                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     } else {
@@ -615,10 +645,12 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         }
 
         __builtin_amdgcn_s_setprio(0);
-        // this wave's loads of the next tile have landed, and after the
-        // barrier every wave's have, and nobody reads the current buffer
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        if constexpr (SYNC) {
+            // this wave's loads of the next tile have landed, and after the
+            // barrier every wave's have, and nobody reads the current buffer
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
     };
 
   for (int item = 0; item < (CAUSAL ? 2 : 1); ++item) {
@@ -707,15 +739,43 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         while (j < ntiles) {
             int jn = next(j);
             bool pn = partial(jn);
-            tile(j, jn, part, pn, std::integral_constant<int, 0>{});
+            tile(j, jn, part, pn, std::integral_constant<int, 0>{}, std::integral_constant<bool, true>{});
             j = jn;
             part = pn;
             if (j >= ntiles) break;
             jn = next(j);
             pn = partial(jn);
-            tile(j, jn, part, pn, std::integral_constant<int, 1>{});
+            tile(j, jn, part, pn, std::integral_constant<int, 1>{}, std::integral_constant<bool, true>{});
             j = jn;
             part = pn;
+        }
+    } else if constexpr (RING == 4) {
+        // Tiles in pairs over a 4-slot ring: tile t sits in slot
+        // (t - jbeg) % 4.  A pair (a, a+1) first issues the loads of a+2 and
+        // a+3 into the slots that a-2 and a-1 left before the last barrier,
+        // computes a and a+1 (the wave's visible ones), and ends with one
+        // barrier.  The pair loop runs over the workgroup's tiles, so every
+        // wave meets the same barriers.
+        const int nt_w = CAUSAL ? min(ntiles, wq_hi / C::BC + 1) : ntiles;
+        if (jbeg < ntiles) load_tile(jbeg, 0, false);
+        if (jbeg + 1 < ntiles) load_tile(jbeg + 1, 1, false);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        auto pair = [&](int a, auto s0_c) __attribute__((always_inline)) {
+            constexpr int S0 = decltype(s0_c)::value;  // slot of tile a: 0 or 2
+            if (a + 2 < ntiles) load_tile(a + 2, (S0 + 2) % 4, false);
+            if (a + 3 < ntiles) load_tile(a + 3, (S0 + 3) % 4, false);
+            if (a < nt_w)
+                tile(a, ntiles, true, true, std::integral_constant<int, S0>{}, std::integral_constant<bool, false>{});
+            if (a + 1 < nt_w)
+                tile(a + 1, ntiles, true, true, std::integral_constant<int, S0 + 1>{},
+                     std::integral_constant<bool, false>{});
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+        for (int a = jbeg; a < ntiles; a += 4) {
+            pair(a, std::integral_constant<int, 0>{});
+            if (a + 2 < ntiles) pair(a + 2, std::integral_constant<int, 2>{});
         }
     } else {
         if (jbeg < ntiles) {
@@ -732,11 +792,11 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         const int nt_w = CAUSAL ? min(ntiles, wq_hi / C::BC + 1) : ntiles;
         int j = jbeg;
         for (; j + 1 < nt_w; j += 2) {
-            tile(j, j + 1, true, true, std::integral_constant<int, 0>{});
-            tile(j + 1, j + 2, true, true, std::integral_constant<int, 1>{});
+            tile(j, j + 1, true, true, std::integral_constant<int, 0>{}, std::integral_constant<bool, true>{});
+            tile(j + 1, j + 2, true, true, std::integral_constant<int, 1>{}, std::integral_constant<bool, true>{});
         }
         if (j < nt_w) {
-            tile(j, j + 1, true, true, std::integral_constant<int, 0>{});
+            tile(j, j + 1, true, true, std::integral_constant<int, 0>{}, std::integral_constant<bool, true>{});
             ++j;
         }
         for (; j < ntiles; ++j) {
