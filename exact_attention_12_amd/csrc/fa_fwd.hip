@@ -161,6 +161,15 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     constexpr int RING = (EXT == 0 && C::NW == 8) ? 4 : 2;
     __shared__ __attribute__((aligned(1024))) char smem[RING * SB];
     poison_lds(smem, sizeof(smem));
+    // Slot placement.  Two slots: K, V (and the mask) of a slot side by side.
+    // Four: the K tiles of all slots first, then the V tiles, so that every
+    // K operand read reaches its slot with the instruction's 16-bit offset
+    // field from one per-lane address, and every V read from another (the
+    // ring spans 128 KiB; a slot-major layout would need an address add per
+    // read of the upper half).
+    static_assert(RING == 2 || (MASKB == 0 && C::ES == 2 && RING * C::TILEB <= 65536), "K slots within 64 KiB");
+    constexpr int KSLOT = RING == 4 ? C::TILEB : SB;  // K tile of slot b at b * KSLOT
+    constexpr int VBASE = RING == 4 ? RING * C::TILEB : C::TILEB;  // V tile of slot b at VBASE + b * KSLOT
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -303,8 +312,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     }
     auto load_tile = [&](int j, int buf, bool with_mask) {
         const int k0 = j * C::BC;
-        char *kd = smem + buf * SB;
-        char *vd = kd + C::TILEB;
+        char *kd = smem + buf * KSLOT;
+        char *vd = smem + VBASE + buf * KSLOT;
         if constexpr (EXT == 4) {
             const uint32_t blk = (uint32_t)trow[min(j * 4 + wave, last_blk)];
             // (block, kv head) slab of 4 KiB; below 4 GiB (checked by the host)
@@ -365,6 +374,19 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
             for (int db = 0; db < C::DB; ++db)
                 v_rd[hi][db] = lds_off(8 * hi + 4 * (g / 2) + r16 / 4,
                                        db * 32 + 16 * (g % 2) + 4 * (r16 % 4));
+    }
+    // Four slots: the V reads add VBASE here, once, in a register the
+    // compiler cannot see through (so it does not fold VBASE back into each
+    // read's offset, past the field's range); Vs below then leaves it out.
+    constexpr int VREG = RING == 4 ? VBASE : 0;
+    if constexpr (RING == 4) {
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+                v_rd[hi][db] += VREG;
+                asm volatile("" : "+v"(v_rd[hi][db]));
+            }
     }
 
     // ---- running state (per lane: one query row, partial over its keys) --
@@ -521,8 +543,8 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
                     for (int g = 0; g < 4; ++g) mcur[kb][g] = all;
             }
         }
-        const char *Ks = smem + STAGE * SB;
-        const char *Vs = Ks + C::TILEB;
+        const char *Ks = smem + STAGE * KSLOT;
+        const char *Vs = smem + VBASE - VREG + STAGE * KSLOT;  // VREG: in v_rd
 
         bool skip = EXT != 0 && (j < jw_beg || j >= jw_end);  // no row of the wave sees a key here
         if constexpr (HAS_MASK) {
