@@ -272,11 +272,21 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
     constexpr int NBQ = BQ / 32;                 // 32-query blocks per tile
     constexpr int QTB = BQ * C::ROWB;            // bytes of a Q or dO tile
     constexpr int STATB = BQ * 4;                // lse2 or D of one tile
-    constexpr int STAGEB = 2 * QTB + 2 * STATB;  // Q, dO, lse2, D
     constexpr int NP = C::QK_STEPS;              // matrix pairs per block, S/dP and dV/dK alike
     static_assert(C::PV_STEPS * C::DB == NP, "S/dP and dV/dK take the same number of pairs");
     using S = DkdvSched<NBQ, NP>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
+    // LDS, two stages: the Q tiles of both in [0, 2 QTB), the dO tiles in
+    // [OBASE, OBASE + 2 QTB), then lse2 and D of stage s at SBASE + 2 STATB s.
+    // A ds_read reaches 64 KiB past its address register with the offset
+    // field; regions beyond that (the dO tiles at d = 128 in 16-bit types, the
+    // statistics) are read from copies of the per-lane offsets that carry the
+    // region's base (OREG, SREG) from setup, kept opaque to the compiler, which
+    // would otherwise fold the base back into each read and add it there.
+    constexpr int OBASE = 2 * QTB, SBASE = 4 * QTB;
+    constexpr int OREG = OBASE + 2 * QTB > 65536 ? OBASE : 0;
+    constexpr int SREG = SBASE;
+    static_assert(2 * QTB <= 65536 && 2 * QTB - OREG <= 65536 && 4 * STATB <= 65536, "regions within reach");
+    __shared__ __attribute__((aligned(1024))) char smem[SBASE + 4 * STATB];
     poison_lds(smem, sizeof(smem));
 
     const int tid = threadIdx.x;
@@ -303,6 +313,24 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
     for (int st = 0; st < C::QK_STEPS; ++st) q_rd[st] = tile_off<C>(col, st * 2 * KW + h * KW);
     int tr[2][C::DB];
     tr_offsets<C>(lane, tr);
+    // the same offsets for the dO tiles (+ OREG), and the statistics' (+ SREG)
+    int o_rd[C::QK_STEPS], tro[2][C::DB];
+#pragma unroll
+    for (int st = 0; st < C::QK_STEPS; ++st) o_rd[st] = q_rd[st] + OREG;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) tro[hi][db] = tr[hi][db] + OREG;
+    if constexpr (OREG != 0) {
+#pragma unroll
+        for (int st = 0; st < C::QK_STEPS; ++st) asm volatile("" : "+v"(o_rd[st]));
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) asm volatile("" : "+v"(tro[hi][db]));
+    }
+    int s_rd = 16 * h + SREG;  // lse2 / D: rows 8i + 4h .. +3 of a 32-row block
+    asm volatile("" : "+v"(s_rd));
 
     const float c = fmaxf(scale * kLog2e, 1e-30f);
     const int nqt = (N + BQ - 1) / BQ;
@@ -346,32 +374,34 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
                 __builtin_amdgcn_make_buffer_rsrc((void *)(Dl + bh * N), 0, N * 4, kBufferFlags);
 
             auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
-                char *qd = smem + buf * STAGEB;
-                ld.load(qrs, qd, wave, j * BQ, N);
-                ld.load(ors, qd + QTB, wave, j * BQ, N);
+                ld.load(qrs, smem + buf * QTB, wave, j * BQ, N);
+                ld.load(ors, smem + OBASE + buf * QTB, wave, j * BQ, N);
                 // lse2 (waves 0, 1) and D (waves 2, 3) of rows j*BQ + 64*(wave%2) + lane;
                 // rows past the end re-read N-1
                 const int r = 64 * (wave % 2) + lane;
-                buffer_load_lds4(wave < 2 ? lrs : drs, qd + 2 * QTB + (wave / 2) * STATB + 64 * 4 * (wave % 2),
+                buffer_load_lds4(wave < 2 ? lrs : drs,
+                                 smem + SBASE + buf * 2 * STATB + (wave / 2) * STATB + 64 * 4 * (wave % 2),
                                  min(j * BQ + r, N - 1) * 4, 0);
             };
 
             // One 32-query block with masks or a causal skip (diagonal and
             // ragged tiles): S/dP, then P/dS, then dV/dK, in sequence.
-            auto masked_block = [&](const char *Qb, const char *Ob, const float *Lb, const float *Db,
+            // Qb: the block's Q rows; Ob, Lb, Db: its dO rows, lse2 and D less
+            // OREG, SREG, SREG (carried by o_rd / tro and s_rd).
+            auto masked_block = [&](const char *Qb, const char *Ob, const char *Lb, const char *Db,
                                     int qf0) __attribute__((always_inline)) {
                 if (CAUSAL && qf0 + 31 < kw0) return;  // every query before every key
                 f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
                 for (int st = 0; st < C::QK_STEPS; ++st) {
                     s = M::mma(*(const frag *)(Qb + q_rd[st]), kf[st], s);
-                    dp = M::mma(*(const frag *)(Ob + q_rd[st]), vf[st], dp);
+                    dp = M::mma(*(const frag *)(Ob + o_rd[st]), vf[st], dp);
                 }
                 f32x4 l4[4], d4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    l4[i] = *(const f32x4 *)(Lb + 8 * i + 4 * h);
-                    d4[i] = *(const f32x4 *)(Db + 8 * i + 4 * h);
+                    l4[i] = *(const f32x4 *)(Lb + 32 * i + s_rd);
+                    d4[i] = *(const f32x4 *)(Db + 32 * i + s_rd);
                 }
                 const int lo = CAUSAL ? key - qf0 - 4 * h : INT_MIN;  // visible iff acc_row(r,0) >= lo
                 const int hi = N - qf0 - 4 * h;                       // ... and acc_row(r,0) < hi
@@ -397,7 +427,7 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
                     const char *qblk = Qb + 16 * st * C::ROWB;
 #pragma unroll
                     for (int db = 0; db < C::DB; ++db) {
-                        dv[db] = M::mma(tr_read<frag>(oblk, tr[0][db], tr[1][db]), pb, dv[db]);
+                        dv[db] = M::mma(tr_read<frag>(oblk, tro[0][db], tro[1][db]), pb, dv[db]);
                         dk[db] = M::mma(tr_read<frag>(qblk, tr[0][db], tr[1][db]), sb, dk[db]);
                     }
                 }
@@ -407,7 +437,7 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
             // schedule above, every LDS operand read two pairs ahead of its
             // use (a ring of three register slots), fenced so that the
             // compiler keeps the order.
-            auto full_tile = [&](const char *Qs, const char *Os, const float *Ls, const float *Ds)
+            auto full_tile = [&](const char *Qs, const char *Os, const char *Ls, const char *Ds)
                 __attribute__((always_inline)) {
                 f32x16 sa[NBQ], da[NBQ];                        // S then P; dP then dS
                 frag pp[NBQ][C::PV_STEPS], sp[NBQ][C::PV_STEPS];  // P, dS packed for the matrix core
@@ -420,10 +450,10 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
                         const char *Qb = Qs + blk * 32 * C::ROWB, *Ob = Os + blk * 32 * C::ROWB;
                         if constexpr (kd == 0) {
                             opr[slot][0] = *(const frag *)(Qb + q_rd[pr]);
-                            opr[slot][1] = *(const frag *)(Ob + q_rd[pr]);
+                            opr[slot][1] = *(const frag *)(Ob + o_rd[pr]);
                         } else {
                             constexpr int st = pr / C::DB, db = pr % C::DB;
-                            opr[slot][0] = tr_read<frag>(Ob + 16 * st * C::ROWB, tr[0][db], tr[1][db]);
+                            opr[slot][0] = tr_read<frag>(Ob + 16 * st * C::ROWB, tro[0][db], tro[1][db]);
                             opr[slot][1] = tr_read<frag>(Qb + 16 * st * C::ROWB, tr[0][db], tr[1][db]);
                         }
                     }
@@ -447,8 +477,8 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
                         static_for<4>([&](auto rc) __attribute__((always_inline)) {
                             constexpr int R = decltype(rc)::value;
                             if constexpr (S::stats_op(B_, R) == G) {
-                                sl[R] = *(const f32x4 *)(Ls + B_ * 32 + 8 * R + 4 * h);
-                                sd[R] = *(const f32x4 *)(Ds + B_ * 32 + 8 * R + 4 * h);
+                                sl[R] = *(const f32x4 *)(Ls + (B_ * 32 + 8 * R) * 4 + s_rd);
+                                sd[R] = *(const f32x4 *)(Ds + (B_ * 32 + 8 * R) * 4 + s_rd);
                             }
                         });
                     });
@@ -491,10 +521,10 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
             auto tile_full = [&](int j, auto stage_c) __attribute__((always_inline)) {
                 constexpr int STAGE = decltype(stage_c)::value;
                 if (j + 1 < nqt) load_tile(j + 1, STAGE ^ 1);
-                const char *Qs = smem + STAGE * STAGEB;
-                const char *Os = Qs + QTB;
-                const float *Ls = (const float *)(Qs + 2 * QTB);
-                full_tile(Qs, Os, Ls, Ls + BQ);
+                const char *Qs = smem + STAGE * QTB;
+                const char *Os = smem + OBASE - OREG + STAGE * QTB;
+                const char *Ls = smem + SBASE - SREG + STAGE * 2 * STATB;
+                full_tile(Qs, Os, Ls, Ls + STATB);
                 // this wave's loads of the next tile have landed, and after the
                 // barrier every wave's have, and nobody reads the current buffer
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -502,13 +532,13 @@ void fa_bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const 
             };
             auto tile_masked = [&](int j, int stage) __attribute__((always_inline)) {
                 if (j + 1 < nqt) load_tile(j + 1, stage ^ 1);
-                const char *Qs = smem + stage * STAGEB;
-                const char *Os = Qs + QTB;
-                const float *Ls = (const float *)(Qs + 2 * QTB);
-                const float *Ds = Ls + BQ;
+                const char *Qs = smem + stage * QTB;
+                const char *Os = smem + OBASE - OREG + stage * QTB;
+                const char *Ls = smem + SBASE - SREG + stage * 2 * STATB;
+                const char *Ds = Ls + STATB;
                 for (int qb = 0; qb < NBQ; ++qb)
-                    masked_block(Qs + qb * 32 * C::ROWB, Os + qb * 32 * C::ROWB, Ls + qb * 32,
-                                 Ds + qb * 32, j * BQ + qb * 32);
+                    masked_block(Qs + qb * 32 * C::ROWB, Os + qb * 32 * C::ROWB, Ls + qb * 32 * 4,
+                                 Ds + qb * 32 * 4, j * BQ + qb * 32);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
             };
