@@ -249,6 +249,20 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     int q0 = 0, qrow = 0, wq_lo = 0, wq_hi = 0, ntiles = 0;
     frag qf[C::QK_STEPS];
 
+    // With a boolean mask at d = 128 in 16-bit types, a wave's live values
+    // exceed the 256 registers it has at two waves per SIMD.  There, values
+    // that are cheap to derive from the lane id are derived again where they
+    // are used (from a copy of the lane id that the compiler cannot hoist)
+    // instead of being held across the key loop, where the register
+    // allocator would spill them: a reload from scratch waits for every load
+    // issued before it, the next tile's prefetch included.
+    constexpr bool TIGHT = HAS_MASK && D == 128 && C::ES == 2;
+    auto lane_id = [&]() __attribute__((always_inline)) {
+        int l = lane;
+        if constexpr (TIGHT) asm volatile("" : "+v"(l));
+        return l;
+    };
+
     // ---- K/V tile j -> LDS buffer buf, straight from global memory --------
     // Load instruction I of a tile fills LDS bytes [I*1024, I*1024 + 1024):
     // lane l writes chunk position q = I*64 + l, i.e. row q / CPR, position
@@ -339,7 +353,9 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
 #pragma unroll
             for (int i = 0; i < C::NLD_W; ++i) {
                 const int I = wave * C::NLD_W + i;
-                const int over = k0 + ld_row[i] - (NK - 1);
+                int row = ld_row[i];
+                if constexpr (TIGHT) row = (I * kWave + lane_id()) / C::CPR;
+                const int over = k0 + row - (NK - 1);
                 const int off = over > 0 ? ld_off[i] - over * C::ROWB : ld_off[i];
                 buffer_load_lds16(krs, kd + I * 1024, off, soff);
                 buffer_load_lds16(vrs, vd + I * 1024, off, soff);
@@ -435,7 +451,9 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
         int last = CAUSAL ? min(qrow, N - 1) : N - 1;
         int first = 0;
         if constexpr (EXT != 0) {
-            const int qr = min(qrow, N - 1);  // rows past the end behave like row N-1
+            int qr = qrow;
+            if constexpr (TIGHT) qr = q0 + wave * 32 + lane_id() % 32;
+            qr = min(qr, N - 1);  // rows past the end behave like row N-1
             last = min(qr + OFF + ext.wr, NK - 1);
             first = qr + OFF - ext.wl;
         }
@@ -448,13 +466,13 @@ void fa_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__
     // mask bytes of keys k0 + kb*32 + 8g + 4h + 0..3 of this lane's row, one
     // dword per (kb, g), from the tile's mask in LDS
     auto read_mask = [&](const char *Ms, uint32_t (&mw)[C::NKB][4]) __attribute__((always_inline)) {
-        const int row = wave * 32 + col;
+        const int l = lane_id(), row = wave * 32 + l % 32, hh = l / 32;
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int chunk = 2 * kb + g / 2;
-                mw[kb][g] = *(const uint32_t *)(Ms + row * C::BC + ((chunk ^ swzm(row)) * 16) + 8 * (g % 2) + 4 * h);
+                mw[kb][g] = *(const uint32_t *)(Ms + row * C::BC + ((chunk ^ swzm(row)) * 16) + 8 * (g % 2) + 4 * hh);
             }
     };
     // returns the visible scores as bits kb*16 + r (used by the boolean mask)
