@@ -941,13 +941,16 @@ hipError_t fwd_dispatch(const void *q, const void *k, const void *v, float *o, f
 // x has a zero byte
 __device__ __forceinline__ bool zero_byte(uint32_t x) { return ((x - 0x01010101u) & ~x & 0x80808080u) != 0; }
 
-// Block map of a boolean mask: one workgroup per (slice, query block qb,
-// word w of 32 key blocks = 2048 keys).  Thread t reads the 16-byte chunk
-// (t % 128) of the word's keys in the 64 rows qb*128 + 64*(t / 128) + ..;
-// bytes past Nk and rows past Nq do not count.  Bit i of the "any" word:
-// key block 32w + i holds a nonzero byte; of the "full" word: it holds no
-// zero byte (and at least one byte, so full implies any).
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+// Block map of a boolean mask: one workgroup of 16 waves per (slice, query
+// block qb, word w of 32 key blocks = 2048 keys).  Thread t reads the
+// 16-byte chunk (t % 128) of the word's keys in the 16 rows qb*128 +
+// 16*(t / 128) + .., all 16 loads at once: the mask is streamed once, and a
+// compute unit needs many loads in flight (four waves of 8-row batches ran
+// at half the speed).  Bytes past Nk and rows past Nq do not count.  Bit i
+// of the "any" word: key block 32w + i holds a nonzero byte; of the "full"
+// word: it holds no zero byte (and at least one byte, so full implies any).
+constexpr int kMapThreads = 1024, kMapRowsPerWave = kMapRows / (kMapThreads / kWave / 2);
+__global__ __attribute__((amdgpu_flat_work_group_size(kMapThreads, kMapThreads)))
 void fa_mask_blocks_kernel(const uint8_t *__restrict__ mask, int Hs, int Nq, int Nk, int64_t msb,
                            int64_t msh, int ldm, int nqb, int nkw, uint32_t *__restrict__ blocks)
 {
@@ -957,10 +960,10 @@ void fa_mask_blocks_kernel(const uint8_t *__restrict__ mask, int Hs, int Nq, int
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c = (wave % 2) * kWave + lane;
-    const int r0 = qb * kMapRows + (wave / 2) * 64;
+    const int r0 = qb * kMapRows + (wave / 2) * kMapRowsPerWave;
     const int key0 = w * 32 * kMapCols + c * 16;
     const int nvalid = min(max(Nk - key0, 0), 16);  // bytes of the chunk inside the key range
-    const int nrows = min(64, Nq - r0);
+    const int nrows = min(kMapRowsPerWave, Nq - r0);
     uint32_t keep[4];  // 0xff on the bytes inside the key range
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -970,13 +973,13 @@ void fa_mask_blocks_kernel(const uint8_t *__restrict__ mask, int Hs, int Nq, int
     bool any = false, all = true;
     if (nvalid > 0 && nrows > 0) {
         const uint8_t *p = base + (int64_t)r0 * ldm + key0;
-        for (int r = 0; r < nrows; r += 8) {
-            u32x4 v[8];
+        for (int r = 0; r < nrows; r += 16) {
+            u32x4 v[16];
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
+            for (int k = 0; k < 16; ++k)
                 if (r + k < nrows) v[k] = *(const u32x4 *)(p + (int64_t)(r + k) * ldm);
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
+            for (int k = 0; k < 16; ++k)
                 if (r + k < nrows) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -994,7 +997,7 @@ void fa_mask_blocks_kernel(const uint8_t *__restrict__ mask, int Hs, int Nq, int
         if ((A >> (4 * i)) & 0xfu) ba |= 1u << i;
         if (((L >> (4 * i)) & 0xfu) == 0xfu) bl |= 1u << i;
     }
-    __shared__ uint32_t sa[4], sl[4];
+    __shared__ uint32_t sa[kMapThreads / kWave], sl[kMapThreads / kWave];
     poison_lds(sa, sizeof(sa));
     poison_lds(sl, sizeof(sl));
     if (lane == 0) {
@@ -1003,8 +1006,17 @@ void fa_mask_blocks_kernel(const uint8_t *__restrict__ mask, int Hs, int Nq, int
     }
     __syncthreads();
     if (tid == 0) {
-        const uint32_t a = (sa[0] | sa[2]) | ((sa[1] | sa[3]) << 16);
-        const uint32_t f = (sl[0] & sl[2]) | ((sl[1] & sl[3]) << 16);
+        // even waves hold key blocks 0..15 of the word, odd waves 16..31
+        uint32_t a0 = 0, a1 = 0, f0 = ~0u, f1 = ~0u;
+#pragma unroll
+        for (int rg = 0; rg < kMapThreads / kWave / 2; ++rg) {
+            a0 |= sa[2 * rg];
+            a1 |= sa[2 * rg + 1];
+            f0 &= sl[2 * rg];
+            f1 &= sl[2 * rg + 1];
+        }
+        const uint32_t a = a0 | (a1 << 16);
+        const uint32_t f = (f0 & 0xffffu) | (f1 << 16);
         uint32_t *out = blocks + ((int64_t)slice * nqb + qb) * 2 * nkw;
         out[w] = a;
         out[nkw + w] = f & a;
@@ -1018,7 +1030,7 @@ hipError_t mask_blocks_dispatch(const uint8_t *mask, int B, int H, int Nq, int N
 {
     const MapShape m = map_shape(B, H, Nq, Nk, msb, msh);
     const int64_t grid = (int64_t)m.Bs * m.Hs * m.nqb * m.nkw;
-    hipLaunchKernelGGL(fa_mask_blocks_kernel, dim3((unsigned)grid), dim3(256), 0, stream, mask, m.Hs, Nq,
+    hipLaunchKernelGGL(fa_mask_blocks_kernel, dim3((unsigned)grid), dim3(kMapThreads), 0, stream, mask, m.Hs, Nq,
                        Nk, msb, msh, ldm, m.nqb, m.nkw, blocks);
     return hipGetLastError();
 }
