@@ -45,6 +45,13 @@ def test_decode_64x32_full(gpu, fa_lib):
     check(inputs.decode_inputs(cfg), cfg, gpu, "64 seqs x 32 heads")
 
 
+def test_decode_gqa_64x32_over_8_full(gpu, fa_lib):
+    # the grouped-query decode as the benchmark runs it: 4 query heads per kv
+    # head (one workgroup per kv head and partition), every row against the oracle
+    cfg = inputs.DECODE_GQA_CONFIG
+    check(inputs.decode_inputs(cfg), cfg, gpu, "64 seqs x 32 heads over 8 kv heads")
+
+
 EDGE_CTX = [0, 1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000, 2049, 4096]
 
 
