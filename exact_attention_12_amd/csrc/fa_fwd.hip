@@ -20,7 +20,8 @@
 //    read patterns below free of bank conflicts.  Double buffered with one
 //    barrier per tile, or, for the 8-wave form, a 4-slot ring whose tiles
 //    go in pairs: a pair loads the next two tiles, computes its two, and
-//    takes one barrier;
+//    takes one barrier (the ring keeps the K tiles of all slots below
+//    64 KiB and the V tiles above, within the LDS reads' offset reach);
 //  - S^T = K Q^T is formed on the matrix cores, so each lane owns one query
 //    row and 16 keys of each 32-key block: the row max and the row sum are
 //    in-lane except for one exchange between the two lane halves;
