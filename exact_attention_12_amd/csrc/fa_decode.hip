@@ -100,41 +100,28 @@ __device__ __forceinline__ void load_block_ids(int (&blk)[NB], const int32_t *__
     for (int i = 0; i < NB; ++i) asm volatile("" : "+s"(blk[i]));
 }
 
-// Every K block of a wave, then every V block (16 bytes per lane per load),
-// as buffer loads that every path issues: a block past the partition's end
-// gets a resource with an empty range (its loads return zeros and touch no
-// memory).  With a fixed count of loads in flight the compiler's waits are
-// exact: the logits of a block wait for its K only, and V keeps arriving
-// meanwhile (1 % faster for four query heads per workgroup; the single-head
-// kernel, with a quarter of the arithmetic per byte, measured 1 % slower
-// with it and keeps its own loads).  The loads are non-temporal: each cache
-// block is read once per call.
+// The blocks of one cache (K or V) that a wave handles, 16 bytes per lane
+// per load, as buffer loads that every path issues: a block past the
+// partition's end gets a resource with an empty range (its loads return
+// zeros and touch no memory).  With a fixed count of loads in flight the
+// compiler's waits are exact.  The loads are non-temporal: each cache block
+// is read once per call.  (The single-head kernel keeps its own loads.)
 template <typename T>
-__device__ __forceinline__ void load_kv_blocks(u32x4 (&kr)[kDecBPW][4], u32x4 (&vr)[kDecBPW][4],
-                                               const T *kc, const T *vc, const int (&blk)[kDecBPW],
-                                               int wave, int nblk, int num_kv_heads, int kvh, int lane)
+__device__ __forceinline__ void load_blocks(u32x4 (&r)[kDecBPW][4], const T *cache, const int (&blk)[kDecBPW],
+                                            int wave, int nblk, int num_kv_heads, int kvh, int lane)
 {
     constexpr int kBlockBytes = kDecD * kDecBS * (int)sizeof(T);
     constexpr int kNonTemporal = 2;  // cache policy bit of the load
-    __amdgpu_buffer_rsrc_t kres[kDecBPW], vres[kDecBPW];
 #pragma unroll
     for (int i = 0; i < kDecBPW; ++i) {
         const bool valid = wave + kDecWaves * i < nblk;
         const int64_t off = valid ? ((int64_t)blk[i] * num_kv_heads + kvh) * (kDecD * kDecBS) : 0;
-        kres[i] = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, valid ? kBlockBytes : 0, kBufferFlags);
-        vres[i] = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, valid ? kBlockBytes : 0, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t res =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(cache + off), 0, valid ? kBlockBytes : 0, kBufferFlags);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            r[i][c] = __builtin_amdgcn_raw_buffer_load_b128(res, (lane + 64 * c) * 16, 0, kNonTemporal);
     }
-#pragma unroll
-    for (int i = 0; i < kDecBPW; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            kr[i][c] = __builtin_amdgcn_raw_buffer_load_b128(kres[i], (lane + 64 * c) * 16, 0, kNonTemporal);
-    __builtin_amdgcn_sched_barrier(0);  // keep every K load ahead of the V loads
-#pragma unroll
-    for (int i = 0; i < kDecBPW; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            vr[i][c] = __builtin_amdgcn_raw_buffer_load_b128(vres[i], (lane + 64 * c) * 16, 0, kNonTemporal);
 }
 
 struct DecWs {
@@ -321,9 +308,10 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
     poison_lds(red, sizeof(red));
     poison_lds(part, sizeof(part));
 
-    // Load order: the queries first, then every K block, then every V block,
-    // so that the queries can be staged and the logits started while V is
-    // still arriving.
+    // Load order: the queries, then the K blocks; the V blocks only after the
+    // logits, into the registers that K leaves free.  Holding both took 156
+    // registers (three workgroups per compute unit); this takes 114 (four),
+    // and the softmax's reductions still overlap V's arrival.
     constexpr int QW = (GM * (kDecD / 2) + kDecThreads - 1) / kDecThreads;  // query words per thread
     uint32_t qw[QW];
 #pragma unroll
@@ -334,7 +322,7 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
         qw[j] = ((const uint32_t *)(q + ((int64_t)s * num_heads + h0) * kDecD))[i];
     }
     u32x4 kr[kDecBPW][4], vr[kDecBPW][4];
-    load_kv_blocks<T>(kr, vr, kc, vc, blk, wave, nblk, num_kv_heads, kvh, lane);
+    load_blocks<T>(kr, kc, blk, wave, nblk, num_kv_heads, kvh, lane);
 #pragma unroll
     for (int j = 0; j < QW; ++j) {
         const int i = tid + j * kDecThreads;
@@ -367,6 +355,7 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
             }
         }
     }
+    load_blocks<T>(vr, vc, blk, wave, nblk, num_kv_heads, kvh, lane);
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
 #pragma unroll
