@@ -100,27 +100,29 @@ __device__ __forceinline__ void load_block_ids(int (&blk)[NB], const int32_t *__
     for (int i = 0; i < NB; ++i) asm volatile("" : "+s"(blk[i]));
 }
 
-// The blocks of one cache (K or V) that a wave handles, 16 bytes per lane
-// per load, as buffer loads that every path issues: a block past the
-// partition's end gets a resource with an empty range (its loads return
-// zeros and touch no memory).  With a fixed count of loads in flight the
-// compiler's waits are exact.  The loads are non-temporal: each cache block
-// is read once per call.  (The single-head kernel keeps its own loads.)
-template <typename T>
-__device__ __forceinline__ void load_blocks(u32x4 (&r)[kDecBPW][4], const T *cache, const int (&blk)[kDecBPW],
+// Blocks i0 .. i0 + NP - 1 of a wave's share (block b = wave + kDecWaves * i
+// of the partition) of one cache, K or V, 16 bytes per lane per load, as
+// buffer loads that every path issues: a block past the partition's end
+// gets a resource with an empty range (its loads return zeros and touch no
+// memory).  With a fixed count of loads in flight the compiler's waits are
+// exact.  The loads are non-temporal: each cache block is read once per
+// call.  (The single-head kernel keeps its own loads.)
+template <typename T, int NP>
+__device__ __forceinline__ void load_blocks(u32x4 (&r)[NP][4], const T *cache, const int (&blk)[kDecBPW], int i0,
                                             int wave, int nblk, int num_kv_heads, int kvh, int lane)
 {
     constexpr int kBlockBytes = kDecD * kDecBS * (int)sizeof(T);
     constexpr int kNonTemporal = 2;  // cache policy bit of the load
 #pragma unroll
-    for (int i = 0; i < kDecBPW; ++i) {
+    for (int ii = 0; ii < NP; ++ii) {
+        const int i = i0 + ii;
         const bool valid = wave + kDecWaves * i < nblk;
         const int64_t off = valid ? ((int64_t)blk[i] * num_kv_heads + kvh) * (kDecD * kDecBS) : 0;
         const __amdgpu_buffer_rsrc_t res =
             __builtin_amdgcn_make_buffer_rsrc((void *)(cache + off), 0, valid ? kBlockBytes : 0, kBufferFlags);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            r[i][c] = __builtin_amdgcn_raw_buffer_load_b128(res, (lane + 64 * c) * 16, 0, kNonTemporal);
+            r[ii][c] = __builtin_amdgcn_raw_buffer_load_b128(res, (lane + 64 * c) * 16, 0, kNonTemporal);
     }
 }
 
@@ -309,9 +311,10 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
     poison_lds(part, sizeof(part));
 
     // Load order: the queries, then the K blocks; the V blocks only after the
-    // logits, into the registers that K leaves free.  Holding both took 156
-    // registers (three workgroups per compute unit); this takes 114 (four),
-    // and the softmax's reductions still overlap V's arrival.
+    // logits, into registers that K leaves free, and in two halves, the
+    // second after the first half's P.V products.  Holding all of K and V
+    // took 156 registers (three workgroups per compute unit); this takes 96
+    // (five), and the softmax's reductions still overlap V's arrival.
     constexpr int QW = (GM * (kDecD / 2) + kDecThreads - 1) / kDecThreads;  // query words per thread
     uint32_t qw[QW];
 #pragma unroll
@@ -321,8 +324,8 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
         const int i = min(tid + j * kDecThreads, ng * (kDecD / 2) - 1);
         qw[j] = ((const uint32_t *)(q + ((int64_t)s * num_heads + h0) * kDecD))[i];
     }
-    u32x4 kr[kDecBPW][4], vr[kDecBPW][4];
-    load_blocks<T>(kr, kc, blk, wave, nblk, num_kv_heads, kvh, lane);
+    u32x4 kr[kDecBPW][4], vr[2][4];
+    load_blocks<T, kDecBPW>(kr, kc, blk, 0, wave, nblk, num_kv_heads, kvh, lane);
 #pragma unroll
     for (int j = 0; j < QW; ++j) {
         const int i = tid + j * kDecThreads;
@@ -355,7 +358,7 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
             }
         }
     }
-    load_blocks<T>(vr, vc, blk, wave, nblk, num_kv_heads, kvh, lane);
+    load_blocks<T, 2>(vr, vc, blk, 0, wave, nblk, num_kv_heads, kvh, lane);  // V blocks 0, 1
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
 #pragma unroll
@@ -395,8 +398,10 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
     for (int g = 0; g < GM; ++g)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[g][c] = 0.f;
+    static_assert(kDecBPW == 4, "V in two halves of two blocks");
 #pragma unroll
     for (int i = 0; i < kDecBPW; ++i) {
+        if (i == 2) load_blocks<T, 2>(vr, vc, blk, 2, wave, nblk, num_kv_heads, kvh, lane);  // V blocks 2, 3
         const int b = wave + kDecWaves * i;
         if (b < nblk) {
             const int tb = b * kDecBS + 8 * (lane % 2);
@@ -405,7 +410,7 @@ void fa_decode_gqa_partition_kernel(const T *__restrict__ q, const T *__restrict
             // hold anything): their value halves are cleared, and p_t = 0
             u32x4 vv[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) vv[c] = vr[i][c];
+            for (int c = 0; c < 4; ++c) vv[c] = vr[i % 2][c];
             if (nvalid < 8) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
